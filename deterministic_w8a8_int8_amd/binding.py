@@ -1,0 +1,198 @@
+"""Thin ctypes binding of libw8a8.so: the same entry points as include/w8a8.h.
+
+Argument marshalling only.  These functions take torch tensors on the GPU,
+allocate outputs the caller did not pass, and hand ``data_ptr()``s and the
+current HIP stream to the C ABI.  Every step of the computation runs in the
+library's gfx950 kernels.  There is no fallback: if the library is missing
+or cannot be loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw8a8.so")
+
+W8A8_OK = 0
+W8A8_ERR_INVALID_ARG = -1
+W8A8_ERR_SHAPE = -2
+W8A8_ERR_ALIGN = -3
+W8A8_ERR_WORKSPACE = -4
+W8A8_ERR_K_BOUND = -5
+W8A8_ERR_TOO_MANY_CANDIDATES = -6
+W8A8_ERR_HIP = -7
+W8A8_MAX_K = 133120
+W8A8_MAX_CANDIDATES = 64
+W8A8_MAX_SPLITK = 64
+
+# Every symbol include/w8a8.h declares, with its ctypes signature.
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "w8a8_status_string": (ctypes.c_char_p, [_I32]),
+    "w8a8_abi_version": (_I32, []),
+    "w8a8_set_tile_override": (_I32, [_I32]),
+    "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
+    "w8a8_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "w8a8_gemm_splitk": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
+    "w8a8_readout_candidates": (_I32, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P]),
+}
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__; __graft_entry__.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = load()
+
+
+def status_string(status: int) -> str:
+    return _lib.w8a8_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib.w8a8_abi_version())
+
+
+def set_tile_override(kind: int) -> None:
+    _check(_lib.w8a8_set_tile_override(int(kind)), "w8a8_set_tile_override")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != W8A8_OK:
+        raise W8A8Error(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+
+
+def w8a8_quantize_act(x, smooth, row_idx=None, xq=None, sx=None, stream=None):
+    """Per-token int8 quantisation of x [rows, K] (row stride may exceed K).
+    Returns (xq int8 [M,K], sx float32 [M]); M = len(row_idx) or rows."""
+    _want(x, torch.float32, "x")
+    _want(smooth, torch.float32, "smooth")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, K = x.shape
+    if row_idx is not None:
+        _want(row_idx, torch.int32, "row_idx")
+        M = row_idx.numel()
+    else:
+        M = rows
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(_lib.w8a8_quantize_act(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth), M, K,
+                                  _ptr(xq), _ptr(sx), _stream(stream)), "w8a8_quantize_act")
+    return xq, sx
+
+
+def _gemm_shapes(xq, sx, w, sw, residual):
+    for t, dt, n in ((xq, torch.int8, "xq"), (sx, torch.float32, "sx"), (w, torch.int8, "w"),
+                     (sw, torch.float32, "sw")):
+        _want(t, dt, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K or sx.numel() != M or sw.numel() != N:
+        raise ValueError("shape mismatch")
+    if residual is not None:
+        _want(residual, torch.float32, "residual")
+        if tuple(residual.shape) != (M, N) or not residual.is_contiguous():
+            raise ValueError("residual must be a contiguous [M, N] float32 tensor")
+    return M, N, K
+
+
+def w8a8_gemm(xq, sx, w, sw, residual=None, y=None, stream=None):
+    """y = fixed epilogue of the exact int32 product xq @ w^T (+ residual)."""
+    M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check(_lib.w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y), M, N, K,
+                          _stream(stream)), "w8a8_gemm")
+    return y
+
+
+def w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) -> int:
+    n = int(_lib.w8a8_gemm_splitk_workspace_bytes(int(M), int(N), int(K), int(splitk)))
+    if n == ctypes.c_size_t(-1).value:
+        raise W8A8Error(W8A8_ERR_INVALID_ARG, "w8a8_gemm_splitk_workspace_bytes")
+    return n
+
+
+def splitk_workspace(M, N, K, splitk, device="cuda"):
+    """A zero-filled workspace of the size w8a8_gemm_splitk needs."""
+    n = w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk)
+    return torch.zeros((max(n, 1),), dtype=torch.uint8, device=device)
+
+
+def w8a8_gemm_splitk(xq, sx, w, sw, splitk, residual=None, y=None, workspace=None, stream=None):
+    """Same result as w8a8_gemm, K split into `splitk` integer partials."""
+    M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if workspace is None:
+        workspace = splitk_workspace(M, N, K, splitk, xq.device)
+    _check(_lib.w8a8_gemm_splitk(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y),
+                                 M, N, K, int(splitk), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "w8a8_gemm_splitk")
+    return y
+
+
+def w8a8_readout_candidates(xq, sx, w_vocab, sw_vocab, cand, logits=None, err_flag=None,
+                            stream=None):
+    """Candidate-only logits [M, C] for vocabulary ids cand [M, C]."""
+    _want(xq, torch.int8, "xq")
+    _want(sx, torch.float32, "sx")
+    _want(w_vocab, torch.int8, "w_vocab")
+    _want(sw_vocab, torch.float32, "sw_vocab")
+    _want(cand, torch.int32, "cand")
+    for t, n in ((xq, "xq"), (w_vocab, "w_vocab"), (cand, "cand")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    M, K = xq.shape
+    V = w_vocab.shape[0]
+    C = cand.shape[1] if cand.dim() == 2 else 0
+    if cand.shape[0] != M:
+        raise ValueError("cand must be [M, C]")
+    if logits is None:
+        logits = torch.empty((M, C), dtype=torch.float32, device=xq.device)
+    _check(_lib.w8a8_readout_candidates(_ptr(xq), _ptr(sx), M, K, _ptr(w_vocab), _ptr(sw_vocab), V,
+                                        _ptr(cand), C, _ptr(logits), _ptr(err_flag), _stream(stream)),
+           "w8a8_readout_candidates")
+    return logits

@@ -1,0 +1,162 @@
+// C ABI of the W8A8 library: argument checks, then dispatch to the gfx950
+// kernels.  Every check that the host can make runs before any launch, and
+// a rejected call changes no output.  Per-entry semantics are documented in
+// include/w8a8.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+#include "w8a8.h"
+
+namespace {
+
+using w8a8::GemmArgs;
+using w8a8::GemmPlan;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_k(int64_t K) {
+    if (K <= 0 || (K % 64) != 0) return W8A8_ERR_SHAPE;
+    if (K > W8A8_MAX_K) return W8A8_ERR_K_BOUND;
+    return W8A8_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;  // grid and index limits of the kernels
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W8A8_OK : W8A8_ERR_HIP; }
+
+// Byte ranges [p, p+n) and [q, q+m) overlap.
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                    const float* residual, float* y, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (M > kMaxDim || N > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!xq || !sx || !w || !sw || !y) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(w, 16) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 4))
+        return W8A8_ERR_ALIGN;
+    if (residual) {
+        if (!aligned(residual, 4)) return W8A8_ERR_ALIGN;
+        const size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
+        if (residual != y && overlaps(residual, bytes, y, bytes)) return W8A8_ERR_INVALID_ARG;
+    }
+    return W8A8_OK;
+}
+
+int run_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+             const float* residual, float* y, int64_t M, int64_t N, int64_t K, int splitk,
+             void* workspace, hipStream_t stream) {
+    if (splitk == 1 && M <= w8a8::SKINNY_MAX_M) {
+        w8a8::SkinnyArgs s{xq, sx, w, sw, residual, y, M, N, K, N, nullptr, N, 0, nullptr};
+        return hip_status(w8a8::launch_skinny(s, stream));
+    }
+    const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
+    const GemmArgs a{xq, sx, w, sw, residual, y, M, N, K};
+    return hip_status(w8a8::launch_gemm_tiled(a, plan, workspace, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w8a8_status_string(int status) {
+    switch (status) {
+        case W8A8_OK: return "ok";
+        case W8A8_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad stride)";
+        case W8A8_ERR_SHAPE: return "unsupported shape (K must be a positive multiple of 64; size limit)";
+        case W8A8_ERR_ALIGN: return "misaligned pointer or stride";
+        case W8A8_ERR_WORKSPACE: return "split-K workspace missing, misaligned or too small";
+        case W8A8_ERR_K_BOUND: return "K above the int32 exactness bound";
+        case W8A8_ERR_TOO_MANY_CANDIDATES: return "too many candidates; use the full-vocabulary GEMM";
+        case W8A8_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+int w8a8_abi_version(void) { return 10000; }
+
+int w8a8_set_tile_override(int kind) {
+    if (kind < -1 || kind > 2) return W8A8_ERR_INVALID_ARG;
+    w8a8::set_tile_override(kind);
+    return W8A8_OK;
+}
+
+int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                      const float* smooth, int64_t M, int64_t K, int8_t* xq, float* sx,
+                      void* stream) {
+    if (M < 0 || x_rows < 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (M > kMaxDim) return W8A8_ERR_SHAPE;
+    if (ldx < K || (ldx % 4) != 0) return W8A8_ERR_INVALID_ARG;
+    if (!row_idx && M > x_rows) return W8A8_ERR_SHAPE;
+    if (M == 0) return W8A8_OK;
+    if (!x || !smooth || !xq || !sx) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(smooth, 16) || !aligned(xq, 16) || !aligned(sx, 4))
+        return W8A8_ERR_ALIGN;
+    if (row_idx && !aligned(row_idx, 4)) return W8A8_ERR_ALIGN;
+    const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx};
+    return hip_status(w8a8::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+              const float* residual, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (const int rc = check_gemm_args(xq, sx, w, sw, residual, y, M, N, K)) return rc;
+    if (M == 0 || N == 0) return W8A8_OK;
+    return run_gemm(xq, sx, w, sw, residual, y, M, N, K, 1, nullptr, static_cast<hipStream_t>(stream));
+}
+
+size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splitk) {
+    if (M < 0 || N < 0 || check_k(K) != W8A8_OK || splitk < 1 || splitk > W8A8_MAX_SPLITK ||
+        M > kMaxDim || N > kMaxDim)
+        return static_cast<size_t>(-1);
+    if (splitk == 1 || M == 0 || N == 0) return 0;
+    return w8a8::gemm_workspace_bytes(w8a8::plan_gemm(M, N, K, splitk));
+}
+
+int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                     const float* residual, float* y, int64_t M, int64_t N, int64_t K, int splitk,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    if (splitk < 1 || splitk > W8A8_MAX_SPLITK) return W8A8_ERR_INVALID_ARG;
+    if (const int rc = check_gemm_args(xq, sx, w, sw, residual, y, M, N, K)) return rc;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (splitk > 1) {
+        const size_t need = w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk);
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W8A8_ERR_WORKSPACE;
+    }
+    return run_gemm(xq, sx, w, sw, residual, y, M, N, K, splitk, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_t K,
+                            const int8_t* w_vocab, const float* sw_vocab, int64_t V,
+                            const int32_t* cand, int64_t C, float* logits, int32_t* err_flag,
+                            void* stream) {
+    if (M < 0 || C < 0 || V <= 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (C > W8A8_MAX_CANDIDATES) return W8A8_ERR_TOO_MANY_CANDIDATES;
+    if (M > kMaxDim || V > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M == 0 || C == 0) return W8A8_OK;
+    if (!xq || !sx || !w_vocab || !sw_vocab || !cand || !logits) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(w_vocab, 16) || !aligned(sx, 4) || !aligned(sw_vocab, 4) ||
+        !aligned(cand, 4) || !aligned(logits, 4))
+        return W8A8_ERR_ALIGN;
+    if (err_flag && !aligned(err_flag, 4)) return W8A8_ERR_ALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // 64 answer rows per launch; each launch gathers M_chunk * C weight rows.
+    for (int64_t m0 = 0; m0 < M; m0 += w8a8::SKINNY_MAX_M) {
+        const int64_t mc = (M - m0 < w8a8::SKINNY_MAX_M) ? (M - m0) : w8a8::SKINNY_MAX_M;
+        w8a8::SkinnyArgs a{xq + m0 * K, sx + m0, w_vocab, sw_vocab, nullptr, logits + m0 * C,
+                           mc, mc * C, K, 0, cand + m0 * C, V, C, err_flag};
+        if (const int rc = hip_status(w8a8::launch_skinny(a, s))) return rc;
+    }
+    return W8A8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Device-side helpers shared by the gfx950 kernels of the W8A8 layer.
+//
+// The fixed binary32 epilogue lives here, once, so the tiled GEMM, the
+// skinny GEMM and the candidate read-out all round the same way.  The
+// review page "StartLux-Prism: Fast, exact inference for StartLux-Decision
+// models on NVIDIA GPUs", section "Bitwise consistency is not lossless
+// quantization", asks for scaling, the residual addition and the read-out
+// to follow one fixed rounding sequence.
+//
+// Every translation unit is compiled with -ffp-contract=off.  The pragma
+// below repeats that, so no multiply-add in these helpers can be fused,
+// whatever flags a user builds with.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace w8a8 {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+
+// y = fl(fl(fl(float(acc)) * sx) * sw): int32 -> binary32 (ties to even,
+// v_cvt_f32_i32), token scale, then channel scale, one rounding each.
+__device__ __forceinline__ float scale_acc(int32_t acc, float sxm, float swn) {
+    const float t0 = static_cast<float>(acc);
+    const float t1 = t0 * sxm;
+    const float t2 = t1 * swn;
+    return t2;
+}
+
+// The same followed by one rounded addition of the residual.
+__device__ __forceinline__ float scale_acc_residual(int32_t acc, float sxm, float swn, float r) {
+    const float t2 = scale_acc(acc, sxm, swn);
+    const float y = t2 + r;
+    return y;
+}
+
+// Quiet NaN for outputs whose inputs were rejected on the device.
+__device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
+
+// Wave64 maximum of a float through cross-lane shuffles (max is exact, so
+// the shuffle order cannot change the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+}  // namespace w8a8

@@ -1,0 +1,80 @@
+// Internal launchers behind the C ABI (host side).  Arguments are validated
+// by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+struct QuantArgs {
+    const float* x;
+    int64_t ldx;
+    int64_t x_rows;
+    const int32_t* row_idx;
+    const float* smooth;
+    int64_t M;
+    int64_t K;
+    int8_t* xq;
+    float* sx;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+    const int8_t* xq;
+    const float* sx;
+    const int8_t* w;
+    const float* sw;
+    const float* residual;
+    float* y;
+    int64_t M;
+    int64_t N;
+    int64_t K;
+};
+
+// Tiled MFMA GEMM.  Which tile shape runs depends only on (M, N, K, splitk);
+// the workspace query and the launch use the same choice.
+enum TileKind { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2 };
+
+struct GemmPlan {
+    TileKind kind;
+    int bm, bn;
+    int64_t tiles_m, tiles_n;
+    int splitk;
+    int group_m;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk);
+void set_tile_override(int kind);
+size_t gemm_workspace_bytes(const GemmPlan& p);
+hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,
+                             hipStream_t stream);
+
+// Skinny-M GEMM (M <= SKINNY_MAX_M): the weight is streamed from HBM once and
+// every wave keeps 16 weight rows against all M activation rows.  With
+// `gather` the weight row of output column j is gather[j]; with owner_c > 0
+// only column j of row j / owner_c is written (the candidate read-out).
+constexpr int64_t SKINNY_MAX_M = 64;
+
+struct SkinnyArgs {
+    const int8_t* xq;
+    const float* sx;
+    const int8_t* w;
+    const float* sw;
+    const float* residual;
+    float* y;
+    int64_t M;
+    int64_t N;       // output columns (gathered rows when gather != nullptr)
+    int64_t K;
+    int64_t ldy;
+    const int32_t* gather;
+    int64_t V;       // rows of w, for bounds checks of gather
+    int64_t owner_c; // 0: plain GEMM; C > 0: read-out, column j belongs to row j / C
+    int32_t* err_flag;
+};
+
+hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+
+}  // namespace w8a8

@@ -1,0 +1,201 @@
+/*
+ * w8a8.h -- C ABI of the deterministic W8A8 int8 linear layer for MI355X (gfx950).
+ *
+ * The layer is the one described on the review page "StartLux-Prism: Fast,
+ * exact inference for StartLux-Decision models on NVIDIA GPUs".  Weights are
+ * int8 with one fp32 scale per output channel.  Activations are divided by a
+ * SmoothQuant per-channel vector and quantised to int8 per token (section
+ * "Compute shared evidence once").  The int8 products accumulate exactly in
+ * int32.  Split-K partial sums stay integers.  A fixed sequence of binary32
+ * operations then applies the scales and the residual (section "Bitwise
+ * consistency is not lossless quantization").  Running the same projection
+ * as a read-out over a few candidate vocabulary rows follows the dsiab.com
+ * post on moving decision models from vLLM to Prism, section "方案": scoring
+ * only the candidates, then normalising among them, equals the
+ * full-vocabulary softmax renormalised over those candidates.
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device.  Host pointers are marked "host".
+ *   - Matrices are row-major.  int8 operands are K-contiguous: the
+ *     activation is [M,K] and the weight is [N,K].
+ *   - `stream` is a hipStream_t passed as void*.  NULL means the default
+ *     stream.  Every compute call is asynchronous on `stream`; no call
+ *     synchronises.
+ *   - The caller owns every buffer, including the split-K workspace.  The
+ *     library allocates no device memory and keeps no per-call state.
+ *   - Host-checkable errors return a negative w8a8_status before anything
+ *     is launched, and leave every output untouched.
+ *   - Determinism: output row m depends only on row m of the inputs and on
+ *     the weights and scales.  It does not depend on M, the row's position,
+ *     other rows, padding, the split-K factor, the kernel or tile the
+ *     library picks, the stream, or the run.  Results are bit-identical to
+ *     the plain definitions written next to each call.
+ *   - Weights must lie in [-127, 127] (the symmetric range), and K <= 133120.
+ *     Then |sum_k q*w| <= K * 127^2 < 2^31, so int32 accumulation is exact.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARG = -1,        /* null pointer, negative size, bad leading dimension */
+    W8A8_ERR_SHAPE = -2,              /* K not a positive multiple of 64, or a size limit */
+    W8A8_ERR_ALIGN = -3,              /* a pointer or stride breaks the stated alignment */
+    W8A8_ERR_WORKSPACE = -4,          /* split-K workspace missing or too small */
+    W8A8_ERR_K_BOUND = -5,            /* K above W8A8_MAX_K: int32 accumulation could overflow */
+    W8A8_ERR_TOO_MANY_CANDIDATES = -6,/* C above W8A8_MAX_CANDIDATES: use the full-vocabulary GEMM */
+    W8A8_ERR_HIP = -7                 /* a HIP launch or runtime call failed */
+} w8a8_status;
+
+/* Largest multiple of 64 with K * 127^2 < 2^31 (the bound is K <= 133144). */
+#define W8A8_MAX_K 133120
+/* Hard cap on candidates per row.  The dsiab.com post (section "复盘", its
+ * closing list of improvements) asks for a cap on the candidate count, with
+ * fallback to the general path above it.  The number 64 is this library's
+ * choice. */
+#define W8A8_MAX_CANDIDATES 64
+/* Largest split-K factor accepted. */
+#define W8A8_MAX_SPLITK 64
+
+/* Human-readable name of a status code (host; never NULL). */
+const char* w8a8_status_string(int status);
+
+/* Version of this ABI: major*10000 + minor*100 + patch (host). */
+int w8a8_abi_version(void);
+
+/* Tuning and test hook (host, process-wide): force the tile shape of the
+ * tiled GEMM for later calls.  -1 = automatic (the default), 0 = 256x256,
+ * 1 = 256x128, 2 = 128x128.  It never changes a result bit, only speed.  It
+ * also changes the split-K workspace size, so query the size again after
+ * changing it.  Returns W8A8_ERR_INVALID_ARG for other values. */
+int w8a8_set_tile_override(int kind);
+
+/*
+ * w8a8_quantize_act -- per-token int8 quantisation after a per-channel
+ * smoothing divide (review page, section "Compute shared evidence once").
+ *
+ * For each output row m, with source row i = row_idx ? row_idx[m] : m, and
+ * fl() meaning one correctly rounded binary32 operation:
+ *     x'[k]  = fl(x[i,k] / smooth[k])                (true IEEE division)
+ *     a      = max_k |x'[k]|
+ *     sx[m]  = fl(a / 127)
+ *     xq[m,k]= clamp(round_half_even(fl(x'[k] / sx[m])), -127, 127),
+ *              or 0 for every k when sx[m] == 0.
+ *
+ * x        device, fp32; row i starts at x + i*ldx; x_rows rows are readable.
+ * ldx      elements between rows, >= K and a multiple of 4.
+ * x_rows   rows of x that may be read; every row_idx entry must lie in [0, x_rows).
+ * row_idx  device int32 [M] or NULL.  NULL requires M <= x_rows.  An entry
+ *          outside [0, x_rows) yields xq[m,:] = 0 and sx[m] = quiet NaN,
+ *          with no out-of-bounds read.
+ * smooth   device fp32 [K], every entry > 0 and finite.
+ * M, K     M >= 0 (M == 0 is a no-op); K a positive multiple of 64, K <= W8A8_MAX_K.
+ * xq       device int8 [M,K] row-major, 16-byte aligned.
+ * sx       device fp32 [M].
+ * Alignment: x and smooth 16-byte aligned.
+ * Non-finite inputs are outside the contract.
+ */
+int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                      const float* smooth, int64_t M, int64_t K,
+                      int8_t* xq, float* sx, void* stream);
+
+/*
+ * w8a8_gemm -- int8 x int8 GEMM with exact int32 accumulation and the fixed
+ * binary32 epilogue (review page, section "Bitwise consistency is not
+ * lossless quantization"):
+ *     acc[m,n] = sum_k xq[m,k] * w[n,k]                         (exact, int32)
+ *     y[m,n]   = fl(fl(fl(float(acc)) * sx[m]) * sw[n])          (+ residual:)
+ *     y[m,n]   = fl(that + residual[m,n])
+ * Each step rounds once (ties to even).  No fused multiply-add is used.
+ * float(acc) is the int32 -> binary32 conversion, ties to even.
+ *
+ * xq        device int8 [M,K], 16-byte aligned (from w8a8_quantize_act).
+ * sx        device fp32 [M].
+ * w         device int8 [N,K], 16-byte aligned, entries in [-127, 127].
+ * sw        device fp32 [N].
+ * residual  device fp32 [M,N] or NULL.  It may be the same pointer as y
+ *           (in-place update of the residual stream), but must not
+ *           otherwise overlap y.
+ * y         device fp32 [M,N], 4-byte aligned.
+ * M, N      >= 0 (an empty output is a no-op).
+ * K         positive multiple of 64, <= W8A8_MAX_K.
+ */
+int w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+              const float* residual, float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * w8a8_gemm_splitk_workspace_bytes -- bytes of device workspace that
+ * w8a8_gemm_splitk needs for this shape and split factor (host; no GPU
+ * call).  Returns 0 when splitk == 1 or the output is empty, and
+ * (size_t)-1 for invalid arguments.
+ */
+size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splitk);
+
+/*
+ * w8a8_gemm_splitk -- the same result as w8a8_gemm, with K cut into
+ * `splitk` contiguous chunks (review page, section "Bitwise consistency is
+ * not lossless quantization": split-K partial sums stay integers).
+ *     chunk c covers k in [c*Kc, min((c+1)*Kc, K)), Kc = ceil(K/splitk)
+ *     rounded up to a multiple of 64;
+ *     P_c[m,n] = sum over chunk c of xq[m,k]*w[n,k]      (int32)
+ *     acc      = P_0 + P_1 + ... + P_{splitk-1}           (int32)
+ * followed by the same epilogue as w8a8_gemm.  No floating-point atomic is
+ * used anywhere.  Partials go through the workspace as int32, and the last
+ * chunk of a tile to finish adds the others onto its own.  Integer addition
+ * is exact and associative, so neither that order nor splitk can change a
+ * bit: the output is bit-identical to w8a8_gemm.
+ *
+ * splitk     1 <= splitk <= W8A8_MAX_SPLITK.
+ * workspace  device, 256-byte aligned, at least
+ *            w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) bytes.
+ *            Its first bytes hold per-tile arrival counters.  They must be
+ *            zero before the first call (allocate with hipMemset or
+ *            torch.zeros).  Every call leaves them zero again.  So one
+ *            workspace serves any later call of the same or smaller size,
+ *            as long as calls that share it do not overlap in time.
+ * Other arguments as for w8a8_gemm.
+ */
+int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                     const float* residual, float* y, int64_t M, int64_t N, int64_t K,
+                     int splitk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w8a8_readout_candidates -- candidate-only lm_head read-out.  The review
+ * page, section "Compute shared evidence once", keeps the read-out to the
+ * answer positions.  The dsiab.com post, section "方案", scores only the
+ * candidate tokens.
+ *     logits[m,c] = fl(fl(float(sum_k xq[m,k]*w_vocab[cand[m,c],k]) * sx[m]) * sw_vocab[cand[m,c]])
+ * This is bit-identical to column cand[m,c] of
+ * w8a8_gemm(xq, sx, w_vocab, sw_vocab, NULL, ...) (no residual).  It runs on
+ * the skinny-GEMM kernel, with the weight rows gathered through `cand`.
+ *
+ * xq, sx      device int8 [M,K] (16-byte aligned) and fp32 [M]; usually the
+ *             answer rows, picked with w8a8_quantize_act's row_idx.
+ * w_vocab     device int8 [V,K], 16-byte aligned; sw_vocab device fp32 [V].
+ * cand        device int32 [M,C]: vocabulary ids, one set per row.  A shared
+ *             set is the same row repeated.
+ * C           0 <= C <= W8A8_MAX_CANDIDATES (above it: W8A8_ERR_TOO_MANY_CANDIDATES,
+ *             use w8a8_gemm over the whole vocabulary instead).
+ * logits      device fp32 [M,C].
+ * err_flag    device int32 or NULL.  An id outside [0,V) makes its logit a
+ *             quiet NaN.  If err_flag is given, bit 0 of *err_flag is set
+ *             (bitwise OR; the library never clears it).
+ */
+int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_t K,
+                            const int8_t* w_vocab, const float* sw_vocab, int64_t V,
+                            const int32_t* cand, int64_t C, float* logits, int32_t* err_flag,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

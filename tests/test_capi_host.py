@@ -1,0 +1,113 @@
+"""The C-ABI library without a GPU.
+
+These checks cover: it loads; it exports every function include/w8a8.h
+declares; and the host-side argument checks reject bad calls before any
+HIP call.  No call here reaches a kernel.  Every rejected call below fails
+validation before the library touches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+LIB = os.path.join(ROOT, "deterministic_w8a8_int8_amd", "libw8a8.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from deterministic_w8a8_int8_amd import build
+        build.build()
+    from deterministic_w8a8_int8_amd import binding
+    return binding._lib
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("w8a8_quantize_act", "w8a8_gemm", "w8a8_gemm_splitk", "w8a8_readout_candidates",
+              "w8a8_gemm_splitk_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from deterministic_w8a8_int8_amd import binding
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version(lib):
+    from deterministic_w8a8_int8_amd import binding as B
+    for s in range(-7, 1):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+    assert B.abi_version() == 10000
+
+
+def test_workspace_query(lib):
+    from deterministic_w8a8_int8_amd import binding as B
+    assert B.w8a8_gemm_splitk_workspace_bytes(8192, 5120, 17408, 1) == 0
+    n2 = B.w8a8_gemm_splitk_workspace_bytes(8192, 5120, 17408, 2)
+    n8 = B.w8a8_gemm_splitk_workspace_bytes(8192, 5120, 17408, 8)
+    # at least S int32 partials of the output plus counters
+    assert n2 >= 2 * 8192 * 5120 * 4 and n8 >= 8 * 8192 * 5120 * 4 and n8 > n2
+    with pytest.raises(B.W8A8Error):
+        B.w8a8_gemm_splitk_workspace_bytes(16, 16, 100, 2)       # K not a multiple of 64
+    with pytest.raises(B.W8A8Error):
+        B.w8a8_gemm_splitk_workspace_bytes(16, 16, 64, 0)
+    with pytest.raises(B.W8A8Error):
+        B.w8a8_gemm_splitk_workspace_bytes(16, 16, 64, 65)
+
+
+def _fake(n=1 << 20, align=256):
+    """A host buffer used only as a non-null, aligned pointer: every call that
+    receives it is rejected before any device access."""
+    buf = ctypes.create_string_buffer(n + align)
+    p = (ctypes.addressof(buf) + align - 1) // align * align
+    return buf, ctypes.c_void_p(p)
+
+
+def test_argument_checks_reject_before_launch(lib):
+    from deterministic_w8a8_int8_amd import binding as B
+    keep, p = _fake()
+    odd = ctypes.c_void_p(p.value + 1)
+    nul = None
+    S = None
+    # quantize: K not multiple of 64, K too large, ldx < K, M > x_rows, null, misaligned
+    assert lib.w8a8_quantize_act(p, 96, 4, nul, p, 4, 96, p, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_quantize_act(p, 133184, 1, nul, p, 1, 133184, p, p, S) == B.W8A8_ERR_K_BOUND
+    assert lib.w8a8_quantize_act(p, 60, 4, nul, p, 4, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_quantize_act(p, 64, 3, nul, p, 4, 64, p, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_quantize_act(nul, 64, 4, nul, p, 4, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_quantize_act(odd, 64, 4, nul, p, 4, 64, p, p, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_quantize_act(p, 64, 4, nul, p, 0, 64, p, p, S) == B.W8A8_OK       # M = 0 no-op
+    # gemm
+    assert lib.w8a8_gemm(p, p, p, p, nul, p, 4, 4, 100, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_gemm(p, p, p, p, nul, p, -1, 4, 64, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_gemm(p, p, odd, p, nul, p, 4, 4, 64, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_gemm(p, p, p, p, nul, nul, 4, 4, 64, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_gemm(p, p, p, p, nul, p, 0, 4, 64, S) == B.W8A8_OK                # empty
+    # residual overlapping y without being y
+    r = ctypes.c_void_p(p.value + 4)
+    assert lib.w8a8_gemm(p, p, p, p, r, p, 4, 4, 64, S) == B.W8A8_ERR_INVALID_ARG
+    # split-K workspace checks
+    assert lib.w8a8_gemm_splitk(p, p, p, p, nul, p, 300, 300, 256, 2, nul, 0, S) == B.W8A8_ERR_WORKSPACE
+    assert lib.w8a8_gemm_splitk(p, p, p, p, nul, p, 300, 300, 256, 2, p, 16, S) == B.W8A8_ERR_WORKSPACE
+    assert lib.w8a8_gemm_splitk(p, p, p, p, nul, p, 300, 300, 256, 2, odd, 1 << 20, S) == B.W8A8_ERR_WORKSPACE
+    assert lib.w8a8_gemm_splitk(p, p, p, p, nul, p, 300, 300, 256, 0, p, 1 << 20, S) == B.W8A8_ERR_INVALID_ARG
+    # read-out
+    assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 65, p, nul, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
+    assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 0, p, 4, p, nul, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 0, p, nul, S) == B.W8A8_OK
+    assert lib.w8a8_set_tile_override(5) == B.W8A8_ERR_INVALID_ARG
+    del keep

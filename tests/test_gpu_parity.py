@@ -1,0 +1,257 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle, bit for bit.
+
+Sizes here let the oracle compute every output in seconds, yet they span
+several tiles, ragged M/N tails, half K-stages, every tile shape, both GEMM
+kernels and several split-K factors.  The workload-sized cases live in
+test_gpu_configs.py.  The definitions come from the review page
+"StartLux-Prism: Fast, exact inference for StartLux-Decision models on NVIDIA
+GPUs", sections "Compute shared evidence once" and "Bitwise consistency is
+not lossless quantization".
+"""
+import numpy as np
+import pytest
+
+import oracle
+from deterministic_w8a8_int8_amd import synth
+from gpu_util import assert_bits_equal, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+from deterministic_w8a8_int8_amd import binding as B  # noqa: E402
+
+
+def _quant_case(M, K, seed, n_out=3, mult=30.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if n_out:
+        x[:, rng.choice(K, n_out, replace=False)] *= np.float32(mult)
+    s = rng.uniform(0.5, 4.0, K).astype(np.float32)
+    return x, s
+
+
+# ------------------------------------------------------------------ quantisation
+
+@pytest.mark.parametrize("M,K", [(1, 64), (16, 256), (37, 1024), (300, 5120), (5, 17408), (2, 40960)])
+def test_quantize_matches_oracle(M, K):
+    say(f"quantize M={M} K={K}")
+    x, s = _quant_case(M, K, seed=M * 7 + K)
+    x[0, :] = 0.0                         # sx = 0 row
+    if M > 1:
+        x[1, :] = 0.0
+        x[1, 3] = np.float32(1e-44)       # amax/127 underflows
+    xq, sx = B.w8a8_quantize_act(dev(x), dev(s))
+    xq_o, sx_o = oracle.quantize_act(x, s)
+    assert_bits_equal(host(sx), sx_o, "sx")
+    np.testing.assert_array_equal(host(xq), xq_o)
+
+
+def test_quantize_ties_and_strides():
+    # rows whose quotients land exactly on .5 (s = 1, amax 127 or 254)
+    K = 128
+    x = np.zeros((4, 256), np.float32)
+    x[0, :8] = [127, 0.5, 1.5, 2.5, -2.5, -0.5, 126.5, 125.5]
+    x[1, :8] = [-254, 1, 3, 5, 7, -3, 253, 0]
+    x[2, :K] = np.arange(K, dtype=np.float32) - 63.5
+    x[3, :K] = 1e-30
+    s = np.ones(K, np.float32)
+    xd = dev(x)[:, 64:64 + K]             # row stride 256 > K
+    xq, sx = B.w8a8_quantize_act(xd, dev(s))
+    xq_o, sx_o = oracle.quantize_act(x[:, 64:64 + K], s)
+    assert_bits_equal(host(sx), sx_o, "sx")
+    np.testing.assert_array_equal(host(xq), xq_o)
+    xq, sx = B.w8a8_quantize_act(dev(x[:, :K]), dev(s))
+    np.testing.assert_array_equal(host(xq)[0, :8], [127, 0, 2, 2, -2, 0, 126, 126])
+    np.testing.assert_array_equal(host(xq)[1, :8], [-127, 0, 2, 2, 4, -2, 126, 0])
+
+
+def test_quantize_row_gather_and_bad_index():
+    x, s = _quant_case(40, 512, seed=5)
+    idx = np.array([39, 0, 17, 17, 5, -1, 40, 2], np.int32)
+    xq, sx = B.w8a8_quantize_act(dev(x), dev(s), row_idx=dev(idx))
+    xq_h, sx_h = host(xq), host(sx)
+    ok = (idx >= 0) & (idx < 40)
+    xq_o, sx_o = oracle.quantize_act(x, s, row_idx=np.where(ok, idx, 0))
+    assert_bits_equal(sx_h[ok], sx_o[ok], "sx")
+    np.testing.assert_array_equal(xq_h[ok], xq_o[ok])
+    assert np.isnan(sx_h[~ok]).all() and not xq_h[~ok].any()
+
+
+# --------------------------------------------------------------------------- GEMM
+
+def _gemm_case(M, N, K, seed, residual):
+    rng = np.random.default_rng(seed)
+    x, s = _quant_case(M, K, seed + 1)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    r = rng.standard_normal((M, N), dtype=np.float32) if residual else None
+    xq, sx = oracle.quantize_act(x, s)
+    return xq, sx, w, sw, r
+
+
+SHAPES = [
+    (1, 7, 64), (3, 256, 320), (16, 256, 256), (64, 130, 192),      # skinny kernel
+    (65, 100, 64), (200, 257, 192), (300, 520, 1024), (513, 264, 320), (256, 256, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("residual", [False, True])
+def test_gemm_matches_oracle(M, N, K, residual):
+    say(f"gemm M={M} N={N} K={K} residual={residual}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + N + K, residual=residual)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+    assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_every_tile_shape_gives_identical_bits(kind):
+    M, N, K = 300, 520, 704
+    say(f"tile kind {kind}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=11, residual=True)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    B.set_tile_override(kind)
+    try:
+        got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+        got_s = host(B.w8a8_gemm_splitk(dev(xq), dev(sx), dev(w), dev(sw), 3, residual=dev(r)))
+    finally:
+        B.set_tile_override(-1)
+    assert_bits_equal(got, want, f"kind {kind}")
+    assert_bits_equal(got_s, want, f"kind {kind} split 3")
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 100, 640), (130, 300, 1024), (257, 513, 1216)])
+@pytest.mark.parametrize("splitk", [2, 3, 4, 8, 13])
+def test_splitk_matches_oracle(M, N, K, splitk):
+    say(f"splitk M={M} N={N} K={K} S={splitk}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=3 * M + N, residual=True)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    ws = B.splitk_workspace(M, N, K, splitk)
+    xq_d, sx_d, w_d, sw_d, r_d = dev(xq), dev(sx), dev(w), dev(sw), dev(r)
+    for rep in range(2):  # the workspace counters must come back to zero
+        got = host(B.w8a8_gemm_splitk(xq_d, sx_d, w_d, sw_d, splitk, residual=r_d, workspace=ws))
+        assert_bits_equal(got, want, f"split {splitk} rep {rep}")
+
+
+def test_splitk_more_chunks_than_kblocks():
+    M, N, K = 70, 90, 192                  # 3 k-blocks, 8 chunks: several are empty
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=77, residual=False)
+    got = host(B.w8a8_gemm_splitk(dev(xq), dev(sx), dev(w), dev(sw), 8))
+    assert_bits_equal(got, oracle.gemm(xq, sx, w, sw), "empty chunks")
+
+
+def test_residual_in_place():
+    M, N, K = 100, 200, 256
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=9, residual=True)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    rd = dev(r)
+    B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=rd, y=rd)
+    assert_bits_equal(host(rd), want, "in place")
+
+
+def test_rows_identical_across_kernels_and_batches():
+    # the same 3 rows alone (skinny kernel), inside a 70-row batch (tiled
+    # kernel), at the end of a 300-row batch, and split 4 ways
+    K, N = 512, 384
+    rng = np.random.default_rng(21)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    x, s = _quant_case(300, K, seed=22)
+    wd, swd, sd = dev(w), dev(sw), dev(s)
+    rows = [297, 298, 299]
+    outs = []
+    for sub in (x[rows], x[230:], x):
+        xq, sx = B.w8a8_quantize_act(dev(sub), sd)
+        outs.append(host(B.w8a8_gemm(xq, sx, wd, swd))[-3:])
+        outs.append(host(B.w8a8_gemm_splitk(xq, sx, wd, swd, 4))[-3:])
+    for o in outs[1:]:
+        assert_bits_equal(o, outs[0], "row invariance")
+    xq_o, sx_o = oracle.quantize_act(x[rows], s)
+    assert_bits_equal(outs[0], oracle.gemm(xq_o, sx_o, w, sw), "vs oracle")
+
+
+def test_repeat_runs_identical():
+    M, N, K = 333, 555, 1088
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=5, residual=True)
+    args = (dev(xq), dev(sx), dev(w), dev(sw))
+    first = host(B.w8a8_gemm(*args, residual=dev(r)))
+    for _ in range(5):
+        assert_bits_equal(host(B.w8a8_gemm(*args, residual=dev(r))), first, "repeat")
+
+
+# ------------------------------------------------------------------------ read-out
+
+def test_readout_equals_full_columns_and_oracle():
+    V, K, M, C = 5000, 512, 3, 4
+    head = synth.lm_head(V=V, K=K, base=55, layer=0)
+    rng = np.random.default_rng(56)
+    h = rng.standard_normal((40, K), dtype=np.float32)
+    answer = np.array([10, 25, 39], np.int32)
+    cand = np.stack([rng.choice(V, C, replace=False) for _ in range(M)]).astype(np.int32)
+    xq, sx = B.w8a8_quantize_act(dev(h), dev(head["smooth"]), row_idx=dev(answer))
+    wd, swd = dev(head["w"]), dev(head["sw"])
+    full = host(B.w8a8_gemm(xq, sx, wd, swd))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    logits = host(B.w8a8_readout_candidates(xq, sx, wd, swd, dev(cand), err_flag=flag))
+    assert host(flag)[0] == 0
+    assert_bits_equal(logits, np.take_along_axis(full, cand.astype(np.int64), 1), "cand vs full")
+    xq_o, sx_o = oracle.quantize_act(h, head["smooth"], row_idx=answer)
+    want, f = oracle.readout_candidates(xq_o, sx_o, head["w"], head["sw"], cand)
+    assert f == 0
+    assert_bits_equal(logits, want, "cand vs oracle")
+
+
+@pytest.mark.parametrize("M,C", [(1, 1), (5, 64), (70, 3), (130, 17)])
+def test_readout_shapes(M, C):
+    V, K = 3000, 256
+    head = synth.lm_head(V=V, K=K, base=57, layer=0)
+    rng = np.random.default_rng(M * C)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    sx = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    cand = rng.integers(0, V, (M, C), dtype=np.int32)
+    got = host(B.w8a8_readout_candidates(dev(xq), dev(sx), dev(head["w"]), dev(head["sw"]), dev(cand)))
+    want, _ = oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
+    assert_bits_equal(got, want, f"readout M={M} C={C}")
+
+
+def test_readout_bad_ids_flagged():
+    V, K = 1000, 128
+    head = synth.lm_head(V=V, K=K, base=58, layer=0)
+    rng = np.random.default_rng(1)
+    xq = rng.integers(-127, 128, (2, K), dtype=np.int8)
+    sx = np.ones(2, np.float32)
+    cand = np.array([[1, V, 3], [-5, 7, 999]], np.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = host(B.w8a8_readout_candidates(dev(xq), dev(sx), dev(head["w"]), dev(head["sw"]), dev(cand),
+                                         err_flag=flag))
+    assert host(flag)[0] == 1
+    assert np.isnan(got[0, 1]) and np.isnan(got[1, 0])
+    want, f = oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
+    ok = ~np.isnan(want)
+    assert_bits_equal(got[ok], want[ok], "good ids")
+
+
+def test_readout_rejects_too_many_candidates():
+    xq = torch.zeros((1, 64), dtype=torch.int8, device="cuda")
+    sx = torch.ones(1, device="cuda")
+    w = torch.zeros((100, 64), dtype=torch.int8, device="cuda")
+    sw = torch.ones(100, device="cuda")
+    cand = torch.zeros((1, 65), dtype=torch.int32, device="cuda")
+    with pytest.raises(B.W8A8Error) as e:
+        B.w8a8_readout_candidates(xq, sx, w, sw, cand)
+    assert e.value.status == B.W8A8_ERR_TOO_MANY_CANDIDATES
+
+
+def test_host_side_errors_leave_outputs_untouched():
+    xq = torch.zeros((4, 96), dtype=torch.int8, device="cuda")       # K = 96: not a multiple of 64
+    sx = torch.ones(4, device="cuda")
+    w = torch.zeros((8, 96), dtype=torch.int8, device="cuda")
+    sw = torch.ones(8, device="cuda")
+    y = torch.full((4, 8), 7.0, device="cuda")
+    with pytest.raises(B.W8A8Error) as e:
+        B.w8a8_gemm(xq, sx, w, sw, y=y)
+    assert e.value.status == B.W8A8_ERR_SHAPE
+    assert (host(y) == 7.0).all()
