@@ -1,0 +1,285 @@
+"""Benchmark of the deterministic W8A8 hot path on one MI355X.
+
+One step is one pass of the whole path over a long-evidence prefill batch
+(M = 8192 tokens, hidden 5120, intermediate 17408, an lm_head of 248000
+rows):
+
+  quantize x [8192,5120]  -> gate+up GEMM  5120 -> 34816
+  quantize h [8192,17408] -> down GEMM    17408 -> 5120, + residual, split-K S
+  quantize the answer row -> candidate read-out, C = 4 lm_head rows
+
+The inputs are seeded synthetic data with the decision model's shapes.  They
+are resident in HBM before the timed region starts.  ``value`` is the int8
+tera-operations (2*M*N*K per GEMM) per second of the whole step.
+``roofline`` is for the dominant kernel (the gate+up GEMM) against the int8
+MFMA peak.  Its duration is measured with HIP events around every launch of
+that kernel inside the timed steps.  ``readout`` reports the full-vocabulary
+skinny GEMM (M = 3 answer rows x 248000 lm_head rows), which is HBM-bound,
+against HBM bandwidth.  That is the general path the candidate read-out
+replaces, timed in the same run.  ``cpu_baseline`` is the CPU oracle on a
+bounded sample of the same step (rank 0 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--splitk S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+METRIC = "W8A8 GEMM TOPS and % int8 MFMA peak (bit-exact); read-out GB/s % HBM"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gemm_tiled": os.path.join(ROOT, "deterministic_w8a8_int8_amd", "csrc", "gemm_tiled.hip"),
+    "gemm_skinny": os.path.join(ROOT, "deterministic_w8a8_int8_amd", "csrc", "gemm_skinny.hip"),
+    "quantize": os.path.join(ROOT, "deterministic_w8a8_int8_amd", "csrc", "quantize.hip"),
+}
+
+
+def source_sha(name: str) -> str:
+    with open(KERNEL_SOURCES[name], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(kernel):
+        return None
+    return t["bytes_per_launch"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--splitk", type=int, default=1, help="split-K factor of the down projection")
+    ap.add_argument("--M", type=int, default=8192, help="prefill tokens")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around kernel launches on the current stream, per name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = fn()
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+        return out
+
+    def mean_us(self, name):
+        ps = self.pairs.get(name, [])
+        return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ps])) if ps else None
+
+    def clear(self):
+        self.pairs = {}
+
+
+def cpu_baseline(gu, dn, head, cand, seconds):
+    """The CPU oracle, untuned, on the first R rows of both layers plus the
+    answer read-out; R grows until the sample costs about `seconds`."""
+    import oracle
+
+    def work(R):
+        t0 = time.perf_counter()
+        xq, sx = oracle.quantize_act(gu["x"][:R], gu["smooth"])
+        oracle.gemm(xq, sx, gu["w"], gu["sw"])
+        xq, sx = oracle.quantize_act(dn["x"][:R], dn["smooth"])
+        y = oracle.gemm(xq, sx, dn["w"], dn["sw"], dn["r"][:R])
+        xq, sx = oracle.quantize_act(y[-1:], head["smooth"])
+        oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
+        return time.perf_counter() - t0
+
+    threads = oracle.num_threads()
+    R = threads
+    dt = work(R)
+    R = int(min(gu["M"], max(threads, threads * round(seconds / max(dt, 1e-3)))))
+    dt = work(R)
+    K1, N1, K2, N2 = gu["K"], gu["N"], dn["K"], dn["N"]
+    ops = 2.0 * R * (N1 * K1 + N2 * K2) + 2.0 * cand.size * head["K"]
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"first {R} of {gu['M']} tokens through both layers plus the read-out "
+                      f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by rows or output columns with no communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from deterministic_w8a8_int8_amd import binding as B
+    from deterministic_w8a8_int8_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    M, S = args.M, args.splitk
+    print(f"# generating inputs (M={M})", file=sys.stderr, flush=True)
+    gu = synth.long_prefill("gate_up", M=M)
+    dn = synth.long_prefill("down", M=M)
+    head = synth.lm_head()
+    rd = synth.readout_inputs()
+    cand1 = rd["cand"][:1]                      # C = 4 candidates for the one answer row
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x1, s1, w1, sw1 = dev(gu["x"]), dev(gu["smooth"]), dev(gu["w"]), dev(gu["sw"])
+    x2, s2, w2, sw2, r2 = dev(dn["x"]), dev(dn["smooth"]), dev(dn["w"]), dev(dn["sw"]), dev(dn["r"])
+    wh, swh, sh = dev(head["w"]), dev(head["sw"]), dev(head["smooth"])
+    cand_d = dev(cand1)
+    answer = torch.tensor([M - 1], dtype=torch.int32, device="cuda")
+    K1, N1, K2, N2 = gu["K"], gu["N"], dn["K"], dn["N"]
+    xq1 = torch.empty((M, K1), dtype=torch.int8, device="cuda")
+    sx1 = torch.empty((M,), dtype=torch.float32, device="cuda")
+    xq2 = torch.empty((M, K2), dtype=torch.int8, device="cuda")
+    sx2 = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((M, N1), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((M, N2), dtype=torch.float32, device="cuda")
+    xq3 = torch.empty((1, K1), dtype=torch.int8, device="cuda")
+    sx3 = torch.empty((1,), dtype=torch.float32, device="cuda")
+    logits = torch.empty((1, cand1.shape[1]), dtype=torch.float32, device="cuda")
+    ws = B.splitk_workspace(M, N2, K2, S) if S > 1 else None
+    timer = Timer(torch)
+
+    def step():
+        timer.run("quantize_h5120", lambda: B.w8a8_quantize_act(x1, s1, xq=xq1, sx=sx1))
+        timer.run("gemm_gate_up", lambda: B.w8a8_gemm(xq1, sx1, w1, sw1, y=y1))
+        timer.run("quantize_h17408", lambda: B.w8a8_quantize_act(x2, s2, xq=xq2, sx=sx2))
+        if S > 1:
+            timer.run("gemm_down", lambda: B.w8a8_gemm_splitk(xq2, sx2, w2, sw2, S, residual=r2, y=y2,
+                                                              workspace=ws))
+        else:
+            timer.run("gemm_down", lambda: B.w8a8_gemm(xq2, sx2, w2, sw2, residual=r2, y=y2))
+        timer.run("quantize_answer", lambda: B.w8a8_quantize_act(y2, sh, row_idx=answer, xq=xq3, sx=sx3))
+        timer.run("readout_candidates",
+                  lambda: B.w8a8_readout_candidates(xq3, sx3, wh, swh, cand_d, logits=logits))
+
+    print("# warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.clear()
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / max(args.steps, 1)
+    ops_step = 2.0 * M * (N1 * K1 + N2 * K2) + 2.0 * cand1.size * K1
+    value = ops_step / (wall / args.steps) / 1e12
+    kernels = {k: round(timer.mean_us(k), 2) for k in timer.pairs}
+
+    # dominant kernel roofline: gate+up GEMM on the int8 MFMA peak
+    gu_us = timer.mean_us("gemm_gate_up")
+    gu_tops = 2.0 * M * N1 * K1 / (gu_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(gu_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(gu_tops / PEAK_INT8_TOPS, 4),
+                "traffic": measured_traffic("gemm_gate_up_long_prefill", "gemm_tiled"),
+                "kernel": "gemm_tiled (256x256 tile)", "shape": [M, N1, K1]}
+    dn_us = timer.mean_us("gemm_down")
+    down = {"us": round(dn_us, 1), "tops": round(2.0 * M * N2 * K2 / (dn_us * 1e-6) / 1e12, 1),
+            "splitk": S}
+    down["frac_mfma"] = round(down["tops"] / PEAK_INT8_TOPS, 4)
+    quant = {}
+    for key, K in (("quantize_h5120", K1), ("quantize_h17408", K2)):
+        us = timer.mean_us(key)
+        gbs = (M * K * 5 + 4 * K + 4 * M) / (us * 1e-6) / 1e9
+        quant[key] = {"us": round(us, 1), "GBs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+    # down projection at other split-K factors (bit-identical output; timed only)
+    split_us = {}
+    for s_ in (1, 2, 4, 8):
+        w_ = B.splitk_workspace(M, N2, K2, s_) if s_ > 1 else None
+        fn = (lambda: B.w8a8_gemm(xq2, sx2, w2, sw2, residual=r2, y=y2)) if s_ == 1 else \
+             (lambda: B.w8a8_gemm_splitk(xq2, sx2, w2, sw2, s_, residual=r2, y=y2, workspace=w_))
+        for _ in range(3):
+            fn()
+        t = Timer(torch)
+        for _ in range(10):
+            t.run("d", fn)
+        torch.cuda.synchronize()
+        split_us[str(s_)] = round(t.mean_us("d"), 1)
+        del w_
+
+    # full-vocabulary read-out (M = 3 answer rows): HBM-bound skinny GEMM
+    Mr = rd["answer_rows"].size
+    xqr, sxr = B.w8a8_quantize_act(dev(rd["h"]), sh, row_idx=dev(rd["answer_rows"]))
+    yfull = torch.empty((Mr, head["N"]), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull)
+    t = Timer(torch)
+    for _ in range(20):
+        t.run("full", lambda: B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull))
+    torch.cuda.synchronize()
+    full_us = t.mean_us("full")
+    full_bytes = head["N"] * head["K"] + 4 * head["N"] + Mr * head["K"] + 4 * Mr + 4 * Mr * head["N"]
+    full_gbs = full_bytes / (full_us * 1e-6) / 1e9
+    readout = {"bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+               "frac": round(full_gbs / PEAK_HBM_GBS, 4), "us": round(full_us, 1),
+               "shape": [int(Mr), head["N"], head["K"]], "kernel": "gemm_skinny",
+               "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
+               "candidate_readout_us": kernels.get("readout_candidates")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(gu, dn, head, cand1, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8 (int32 accumulate, fp32 epilogue)",
+        "data": "synthetic",
+        "config": {"workload": "long-evidence prefill", "M": M, "hidden": K1, "gate_up": N1,
+                   "intermediate": K2, "down": N2, "splitk_down": S, "lm_head_rows": head["N"],
+                   "candidates": int(cand1.shape[1]), "answer_rows": 1},
+        "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
+        "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy probe: {n} bytes read and {n} bytes written per copy, 3 copies",
+              file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()
