@@ -16,8 +16,12 @@ MFMA peak.  Its duration is measured with HIP events around every launch of
 that kernel inside the timed steps.  ``readout`` reports the full-vocabulary
 skinny GEMM (M = 3 answer rows x 248000 lm_head rows), which is HBM-bound,
 against HBM bandwidth.  That is the general path the candidate read-out
-replaces, timed in the same run.  ``cpu_baseline`` is the CPU oracle on a
-bounded sample of the same step (rank 0 only).
+replaces, timed in the same run.  ``mfma_ceiling`` is the throughput the
+int8 matrix cores sustain on register-resident operands with no memory
+traffic (uniform int8, and activation-like A), measured in the same run;
+``roofline.frac_of_sustained_ceiling`` relates the GEMM to the second.
+``cpu_baseline`` is the CPU oracle on a bounded sample of the same step
+(rank 0 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--splitk S]
 """
@@ -252,6 +256,21 @@ def main():
                "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
                "candidate_readout_us": kernels.get("readout_candidates")}
 
+    # sustained MFMA-only ceiling on this GPU for two kinds of operand data
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    ceiling = {}
+    for kind, name in ((0, "uniform_int8"), (1, "activation_like")):
+        B.w8a8_probe_mfma_ceiling(kind, 1024, 50, sink)
+        best = 0.0
+        for _ in range(3):
+            t = Timer(torch)
+            ops = t.run("c", lambda: B.w8a8_probe_mfma_ceiling(kind, 1024, 1500, sink))
+            torch.cuda.synchronize()
+            best = max(best, ops / (t.mean_us("c") * 1e-6) / 1e12)
+        ceiling[name + "_TOPS"] = round(best, 1)
+    roofline["sustained_mfma_ceiling_TOPS"] = ceiling["activation_like_TOPS"]
+    roofline["frac_of_sustained_ceiling"] = round(gu_tops / ceiling["activation_like_TOPS"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -267,6 +286,7 @@ def main():
                    "candidates": int(cand1.shape[1]), "answer_rows": 1},
         "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
+        "mfma_ceiling": ceiling,
     }
     print(json.dumps(line), flush=True)
 

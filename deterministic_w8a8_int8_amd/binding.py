@@ -34,6 +34,7 @@ SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [_I32]),
     "w8a8_abi_version": (_I32, []),
     "w8a8_set_tile_override": (_I32, [_I32]),
+    "w8a8_probe_mfma_ceiling": (_I32, [_I32, _I64, _I64, _P, _P, _P]),
     "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "w8a8_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
@@ -74,6 +75,14 @@ def abi_version() -> int:
 
 def set_tile_override(kind: int) -> None:
     _check(_lib.w8a8_set_tile_override(int(kind)), "w8a8_set_tile_override")
+
+
+def w8a8_probe_mfma_ceiling(operand_kind, blocks, iters, sink, stream=None) -> int:
+    """Launch the MFMA-only diagnostic kernel; returns the int8 ops launched."""
+    ops = ctypes.c_int64(0)
+    _check(_lib.w8a8_probe_mfma_ceiling(int(operand_kind), int(blocks), int(iters), _ptr(sink),
+                                        ctypes.byref(ops), _stream(stream)), "w8a8_probe_mfma_ceiling")
+    return ops.value
 
 
 def _check(rc: int, what: str) -> None:

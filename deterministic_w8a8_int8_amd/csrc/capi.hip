@@ -83,9 +83,19 @@ const char* w8a8_status_string(int status) {
 int w8a8_abi_version(void) { return 10000; }
 
 int w8a8_set_tile_override(int kind) {
-    if (kind < -1 || kind > 2) return W8A8_ERR_INVALID_ARG;
+    if (kind < -1 || kind >= w8a8::TILE_KINDS) return W8A8_ERR_INVALID_ARG;
     w8a8::set_tile_override(kind);
     return W8A8_OK;
+}
+
+int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
+                            int64_t* ops, void* stream) {
+    if ((operand_kind != 0 && operand_kind != 1) || blocks <= 0 || blocks > kMaxDim || iters <= 0 ||
+        !sink || !aligned(sink, 4))
+        return W8A8_ERR_INVALID_ARG;
+    if (ops) *ops = w8a8::mfma_ceiling_ops(blocks, iters);
+    return hip_status(w8a8::launch_mfma_ceiling(operand_kind, blocks, iters, sink,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,

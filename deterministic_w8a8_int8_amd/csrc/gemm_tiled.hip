@@ -9,19 +9,22 @@
 // floating-point atomic appears anywhere: the float atomic accumulation that
 // page describes flipped a near-tie decision between runs.
 //
-// Design (CDNA4, wave64):
-//   - 256 threads = 4 waves in a 2 x 2 arrangement.  Each wave owns a
-//     (32*WTM) x (32*WTN) block of the output as WTM*WTN accumulators of
-//     v_mfma_i32_32x32x32_i8 (16 int32 per lane each).
+// Design (CDNA4, wave64).  One kernel template, several tile configurations
+// (Cfg below); results never depend on the configuration:
+//   - WGM x WGN waves per workgroup.  Each wave owns a (32*WTM) x (32*WTN)
+//     block of the output as WTM*WTN accumulators of v_mfma_i32_32x32x32_i8
+//     (16 int32 per lane each, held in AGPRs).
 //   - Both operands are K-contiguous (activation [M,K], weight [N,K]).  One
-//     K stage is 128 bytes per row: one cache line of every row of the tile.
-//     It is copied HBM -> LDS with global_load_lds_dwordx4, which needs no
-//     VGPR staging.  Each wave instruction fills 1 KiB of LDS = 8 rows.
-//   - LDS holds two stages (double buffer).  Stage s+1 is in flight while
-//     the MFMAs consume stage s.  There is one barrier per stage.
-//   - 16-byte chunks of a row are XOR-swizzled with (row & 7) ^ ((row >> 3) & 1).
-//     Then the 8- or 16-lane groups that a ds_read_b128 serves together hit
-//     distinct banks, for either 32 or 64 LDS banks.
+//     K stage is BK bytes (64 or 128) of every row of the tile.  It is
+//     copied HBM -> LDS with global_load_lds_dwordx4, which needs no VGPR
+//     staging.  Each wave instruction fills 1 KiB of LDS.
+//   - NST LDS stages.  NST - 1 stages are being copied in while one is
+//     multiplied.  There is one barrier per stage.  Configurations with two
+//     waves per SIMD (8 waves, or 2 workgroups per CU) let one wave issue
+//     MFMAs while the other waits on LDS, a barrier or its epilogue.
+//   - 16-byte chunks of a row are XOR-swizzled (row_swz).  Then the 8- or
+//     16-lane groups that a ds_read_b128 serves together hit distinct banks,
+//     for either 32 or 64 LDS banks.
 //   - Integer accumulation is exact, so any lane -> k assignment gives the
 //     same sum, provided A and B use the same one.  Only the placement of the
 //     32 x 32 result tile matters.
@@ -46,20 +49,41 @@ namespace w8a8 {
 
 namespace {
 
-constexpr int BK = 128;        // K bytes per stage
-constexpr int THREADS = 256;   // 4 waves
 constexpr int NXCD = 8;        // XCDs on MI355X
 
-template <int WTM, int WTN>
-struct Tile {
-    static constexpr int BM = 64 * WTM;
-    static constexpr int BN = 64 * WTN;
+// A tile configuration.
+//   WGM x WGN   waves per workgroup        WTM x WTN  32x32 MFMA tiles per wave
+//   BK_         K bytes per LDS stage      NST_       LDS stages
+//   OCC_        workgroups per CU the register budget is sized for
+template <int WGM_, int WGN_, int WTM_, int WTN_, int BK_, int NST_, int OCC_, bool DIRECT_EPI_ = false>
+struct Cfg {
+    static constexpr bool DIRECT_EPI = DIRECT_EPI_;
+    static constexpr int WGM = WGM_, WGN = WGN_, WTM = WTM_, WTN = WTN_;
+    static constexpr int NW = WGM * WGN;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int BM = 32 * WTM * WGM;
+    static constexpr int BN = 32 * WTN * WGN;
+    static constexpr int BK = BK_;
+    static constexpr int NST = NST_;
+    static constexpr int OCC = OCC_;
+    static constexpr int CHUNKS = BK / 16;            // 16-byte chunks per LDS row
+    static constexpr int ROWS_PER_FILL = 64 / CHUNKS; // rows one wave instruction fills
     static constexpr int A_BYTES = BM * BK;
     static constexpr int B_BYTES = BN * BK;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = BM / 32;   // 8 rows per wave instruction, 4 waves
-    static constexpr int B_LOADS = BN / 32;
+    static constexpr int A_LOADS = BM / (ROWS_PER_FILL * NW);
+    static constexpr int B_LOADS = BN / (ROWS_PER_FILL * NW);
+    static constexpr int LPS = A_LOADS + B_LOADS;     // fill instructions per wave per stage
+    static constexpr int SUBSTEPS = BK / 32;          // MFMA K-steps per stage
     static constexpr int ACC_PER_WAVE = WTM * WTN * 16 * 64;  // int32 per wave
+    static constexpr int STAGED_ROWS = 32 * WGM;      // epilogue rows per pass
+    static constexpr int LDR = BN + 8;                // staged row pitch (int32)
+    static constexpr int EPI_BYTES = STAGED_ROWS * LDR * 4 + (BM + BN) * 4;
+    static constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
+    static_assert(A_LOADS * ROWS_PER_FILL * NW == BM && B_LOADS * ROWS_PER_FILL * NW == BN,
+                  "fills must cover the tile");
+    static_assert(NST >= 2 && NST <= 4, "pipeline depth");
+    static_assert(THREADS % (BN / 4) == 0, "epilogue sweep");
 };
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -67,7 +91,7 @@ typedef __attribute__((address_space(3))) int8_t lds_i8;
 // One wave instruction: every lane copies 16 bytes from gbase + voff into LDS
 // at lds + 16*lane (global_load_lds_dwordx4; the LDS base goes through M0).
 // Issued as inline asm so that the compiler does not make later LDS reads of
-// the other buffer wait for this copy; the caller waits with vmcnt(0)
+// other buffers wait for this copy; the kernel waits with an explicit vmcnt
 // before the barrier that publishes the stage.
 __device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -78,21 +102,47 @@ __device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, l
 
 __device__ __forceinline__ void wait_fills() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// v_mfma_i32_32x32x32_i8 as inline asm: C += A * B on one 32x32 int32 tile
+// held in AGPRs.  The memory clobber pins it in program order relative to
+// the LDS reads and fills around it (the instruction schedule of the main
+// loop is written in the source).
+__device__ __forceinline__ void mfma_32x32x32_i8(i32x16& c, const i32x4& a, const i32x4& b) {
+    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+}
+
+// Generous wait states after the last MFMA before its results are read by
+// other instructions (an MFMA written in inline asm is not tracked by the
+// compiler's hazard recognizer in every case).
+__device__ __forceinline__ void mfma_drain() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // Keeps the scheduler from mixing the work of neighbouring output tiles,
 // which bounds register pressure in the epilogue.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
-// Swizzle of the 16-byte chunk index inside a 128-byte LDS row.
-__device__ __forceinline__ int row_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Swizzle of the 16-byte chunk index inside an LDS row of CHUNKS chunks.
+// Rows r..r+15 read at one logical chunk land in 16 distinct 16-byte bank
+// groups of a 256-byte window (64 banks), and rows r..r+7 in 8 distinct
+// groups of a 128-byte window (32 banks).
+template <int CHUNKS>
+__device__ __forceinline__ int row_swz(int r) {
+    if constexpr (CHUNKS == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else return ((r >> 1) & 3) ^ (((r >> 3) & 1) * 3);
+}
 
-template <int WTM, int WTN>
-__global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, const float* residual, float* y, int M, int N, int K,
     int tiles_m, int tiles_n, int group_m, int splitk, int kb_per_split,
     int32_t* __restrict__ counters, int32_t* __restrict__ partials) {
-    using T = Tile<WTM, WTN>;
-    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * T::STAGE];
+    constexpr int WTM = C::WTM, WTN = C::WTN, BK = C::BK, NST = C::NST;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS_BYTES];
     __shared__ int last_flag;
 
     // ---- block -> (tile, split), XCD-contiguous and grouped along M
@@ -112,69 +162,75 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
     const int tm = first_m + in_g % gm;
     const int tn = in_g / gm;
 
-    const int row0 = tm * T::BM;
-    const int col0 = tn * T::BN;
-    const int KB = K >> 6;                               // 64-byte k-blocks
+    const int row0 = tm * C::BM;
+    const int col0 = tn * C::BN;
+    const int KB = K >> 6;                       // 64-byte k-blocks
     const int kb0 = min(split * kb_per_split, KB);
     const int kb1 = min(kb0 + kb_per_split, KB);
     const int nkb = kb1 - kb0;
-    const int nst = (nkb + 1) >> 1;                      // stages (last may be half)
-    const bool half_last = (nkb & 1) != 0;
+    constexpr int KB_PER_STAGE = BK / 64;
+    const int nst = (nkb + KB_PER_STAGE - 1) / KB_PER_STAGE;
+    const bool half_last = (nkb % KB_PER_STAGE) != 0;   // only with BK = 128
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-    // ---- per-lane global offsets for the LDS fills
-    // Instruction j of wave w fills LDS rows 8*(w + 4j) .. +7; lane l lands in
-    // row 8*(w+4j) + l/8 at physical chunk l%8, which holds logical chunk
-    // (l%8) ^ swz(row).
-    // With r = 8*(w+4j) + l/8: r & 7 = l/8 and (r >> 3) & 1 = w & 1, so the
-    // logical chunk a lane fetches is the same for every j.
-    const int lrow = lane >> 3;
-    const int lchunk = (lane & 7) ^ lrow ^ (wave & 1);
-    uint32_t a_off[T::A_LOADS], b_off[T::B_LOADS];
+    // ---- per-lane global offsets for the LDS fills.  Instruction j of wave w
+    // fills LDS rows RPF*(w + NW*j) .. +RPF-1 (RPF = rows per fill, 1 KiB);
+    // lane l lands in row RPF*(w + NW*j) + l / CHUNKS at physical chunk
+    // l % CHUNKS, which holds logical chunk (l % CHUNKS) ^ swz(row).
+    constexpr int RPF = C::ROWS_PER_FILL;
+    const int lrow = lane / C::CHUNKS;
+    const int lphys = lane % C::CHUNKS;
+    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+    int a_chunk[C::A_LOADS], b_chunk[C::B_LOADS];
 #pragma unroll
-    for (int j = 0; j < T::A_LOADS; ++j) {
-        const int r = 8 * (wave + 4 * j) + lrow;
+    for (int j = 0; j < C::A_LOADS; ++j) {
+        const int r = RPF * (wave + C::NW * j) + lrow;
         const int gr = min(row0 + r, M - 1);
+        a_chunk[j] = lphys ^ row_swz<C::CHUNKS>(r);
         a_off[j] = static_cast<uint32_t>(gr - row0) * static_cast<uint32_t>(K) +
-                   static_cast<uint32_t>(lchunk * 16);
+                   static_cast<uint32_t>(a_chunk[j] * 16);
     }
 #pragma unroll
-    for (int j = 0; j < T::B_LOADS; ++j) {
-        const int r = 8 * (wave + 4 * j) + lrow;
+    for (int j = 0; j < C::B_LOADS; ++j) {
+        const int r = RPF * (wave + C::NW * j) + lrow;
         const int gc = min(col0 + r, N - 1);
+        b_chunk[j] = lphys ^ row_swz<C::CHUNKS>(r);
         b_off[j] = static_cast<uint32_t>(gc - col0) * static_cast<uint32_t>(K) +
-                   static_cast<uint32_t>(lchunk * 16);
+                   static_cast<uint32_t>(b_chunk[j] * 16);
     }
     const int8_t* a_base = A + static_cast<int64_t>(row0) * K + kb0 * 64;
     const int8_t* b_base = B + static_cast<int64_t>(col0) * K + kb0 * 64;
 
     auto issue = [&](int st, int buf) {
-        // In a half stage the upper 64 bytes may lie past the chunk (or the
-        // matrix): fold those lanes onto the lower half, whose bytes are valid.
+        // A half stage (BK = 128, odd number of k-blocks) must not read past
+        // the chunk or the matrix: lanes of the upper half re-read the lower
+        // half, whose bytes are valid and are never multiplied.
         const bool half = half_last && (st == nst - 1);
-        const uint32_t fold = (half && lchunk >= 4) ? 64u : 0u;
         const int8_t* ga = a_base + st * BK;
         const int8_t* gb = b_base + st * BK;
-        lds_i8* la = (lds_i8*)smem + buf * T::STAGE + 8 * wave * BK;
-        lds_i8* lb = la + T::A_BYTES;
+        lds_i8* la = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK;
+        lds_i8* lb = la + C::A_BYTES;
 #pragma unroll
-        for (int j = 0; j < T::A_LOADS; ++j) lds_fill16(ga, a_off[j] - fold, la + 32 * j * BK);
+        for (int j = 0; j < C::A_LOADS; ++j)
+            lds_fill16(ga, a_off[j] - ((half && a_chunk[j] >= 4) ? 64u : 0u), la + RPF * C::NW * j * BK);
 #pragma unroll
-        for (int j = 0; j < T::B_LOADS; ++j) lds_fill16(gb, b_off[j] - fold, lb + 32 * j * BK);
+        for (int j = 0; j < C::B_LOADS; ++j)
+            lds_fill16(gb, b_off[j] - ((half && b_chunk[j] >= 4) ? 64u : 0u), lb + RPF * C::NW * j * BK);
     };
 
-    // ---- per-lane LDS read offsets for the MFMA operands
-    // Fragment i of this wave: rows wm*32*WTM + 32*i + (lane & 31); K sub-step
-    // s (32 bytes) uses logical chunk 2s + (lane >> 5).
-    const int rsw = row_swz(lane & 31);
+    // ---- per-lane LDS read offsets for the MFMA operands.  Fragment i of this
+    // wave covers rows wm*32*WTM + 32*i + (lane & 31); K sub-step s (32 bytes)
+    // uses logical chunk 2s + (lane >> 5).  Those rows are congruent to
+    // lane & 15 modulo 16, which fixes the swizzle.
+    const int rsw = row_swz<C::CHUNKS>(lane & 15);
     const int a_row_off = (wm * 32 * WTM + (lane & 31)) * BK;
     const int b_row_off = (wn * 32 * WTN + (lane & 31)) * BK;
-    int chunk_off[4];
+    int chunk_off[C::SUBSTEPS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) chunk_off[s] = ((2 * s + (lane >> 5)) ^ rsw) * 16;
+    for (int s = 0; s < C::SUBSTEPS; ++s) chunk_off[s] = ((2 * s + (lane >> 5)) ^ rsw) * 16;
 
     i32x16 acc[WTM][WTN];
 #pragma unroll
@@ -184,42 +240,182 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    auto substep = [&](const int8_t* la, const int8_t* lb, int s) {
+    // Fragments of one 32-byte K sub-step: WTM activation and WTN weight
+    // fragments, 16 bytes per lane each.
+    struct Frags {
         i32x4 a[WTM], b[WTN];
-#pragma unroll
-        for (int i = 0; i < WTM; ++i)
-            a[i] = *reinterpret_cast<const i32x4*>(la + a_row_off + i * 32 * BK + chunk_off[s]);
-#pragma unroll
-        for (int j = 0; j < WTN; ++j)
-            b[j] = *reinterpret_cast<const i32x4*>(lb + b_row_off + j * 32 * BK + chunk_off[s]);
-#pragma unroll
-        for (int i = 0; i < WTM; ++i)
-#pragma unroll
-            for (int j = 0; j < WTN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
+    auto load_frag = [&](Frags& f, const int8_t* la, const int8_t* lb, int s, int q) {
+        if (q < WTM)
+            f.a[q] = *reinterpret_cast<const i32x4*>(la + a_row_off + q * 32 * BK + chunk_off[s]);
+        else
+            f.b[q - WTM] =
+                *reinterpret_cast<const i32x4*>(lb + b_row_off + (q - WTM) * 32 * BK + chunk_off[s]);
+    };
+    // One fill instruction of stage st into buffer buf: index d over the A
+    // fills, then the B fills.
+    auto issue_one = [&](int st, int buf, int d) {
+        const bool half = half_last && (st == nst - 1);
+        lds_i8* la = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK;
+        if (d < C::A_LOADS) {
+            lds_fill16(a_base + st * BK, a_off[d] - ((half && a_chunk[d] >= 4) ? 64u : 0u),
+                       la + RPF * C::NW * d * BK);
+        } else {
+            const int e = d - C::A_LOADS;
+            lds_fill16(b_base + st * BK, b_off[e] - ((half && b_chunk[e] >= 4) ? 64u : 0u),
+                       la + C::A_BYTES + RPF * C::NW * e * BK);
+        }
     };
 
-    if (nst > 0) issue(0, 0);
-    for (int st = 0; st < nst; ++st) {
-        wait_fills();     // this wave's copies of stage st have landed
-        __syncthreads();  // ... and every wave's; buffer (st+1)&1 is free again
-        if (st + 1 < nst) issue(st + 1, (st + 1) & 1);
-        const int8_t* la = smem + (st & 1) * T::STAGE;
-        const int8_t* lb = la + T::A_BYTES;
-        substep(la, lb, 0);
-        substep(la, lb, 1);
-        if (!(half_last && st == nst - 1)) {
-            substep(la, lb, 2);
-            substep(la, lb, 3);
+    // ---- main loop: NST - 1 stages in flight.  At iteration st the wave waits
+    // until its copies of stage st have landed (later stages may still be
+    // pending); the barrier publishes stage st to every wave and frees the
+    // buffer of stage st - 1, into which stage st + NST - 1 is copied while
+    // stage st is multiplied.
+    //
+    // Instruction schedule of one stage (the MFMA is inline asm with a memory
+    // clobber, so MFMAs, LDS reads and fills stay in this order): after each
+    // MFMA of sub-step s the wave issues one LDS read of a sub-step s+1
+    // fragment and, during the first sub-steps, one fill instruction of the
+    // next stage.  Those issue in the shadow of the running MFMA instead of
+    // stalling the matrix core in a block of their own.
+    if constexpr (NST >= 3) {
+        // Publish-ahead pipeline (64-byte stages).  The barrier of iteration
+        // st publishes stage st+1 and frees the buffer of stage st-1, into
+        // which stage st + NST - 1 is copied.  The first fragments of each
+        // stage are read during the previous stage's last MFMAs, so no stage
+        // starts with the matrix core waiting on LDS.
+        static_assert(C::SUBSTEPS == 2, "publish-ahead pipeline uses 64-byte stages");
+#pragma unroll
+        for (int p = 0; p < NST - 1; ++p)
+            if (p < nst) issue(p, p);
+        Frags f0, f1;
+        if (nst > 0) {
+            const int pend0 = min(NST - 2, nst - 1);              // stages issued after stage 0
+            if (pend0 >= 2) wait_vm<2 * C::LPS>();
+            else if (pend0 == 1) wait_vm<C::LPS>();
+            else wait_vm<0>();
+            __syncthreads();
+            const int8_t* la = smem;
+#pragma unroll
+            for (int q = 0; q < WTM + WTN; ++q) load_frag(f0, la, la + C::A_BYTES, 0, q);
+        }
+        for (int st = 0; st < nst; ++st) {
+            const bool more = st + 1 < nst;
+            const bool fill = st + NST - 1 < nst;
+            if (more) {
+                const int pend = min(st + NST - 2, nst - 1) - (st + 1);   // issued after st+1
+                if constexpr (NST >= 4) {
+                    if (pend >= 1) wait_vm<C::LPS>();
+                    else wait_vm<0>();
+                } else {
+                    wait_vm<0>();
+                }
+                __syncthreads();
+            }
+            const int8_t* la = smem + (st % NST) * C::STAGE;
+            const int8_t* lb = la + C::A_BYTES;
+            const int8_t* la_n = smem + ((st + 1) % NST) * C::STAGE;
+            const int8_t* lb_n = la_n + C::A_BYTES;
+            int q = 0, d = 0;
+            // sub-step 0: MFMAs on f0; read sub-step 1 into f1; copy stage st+NST-1
+#pragma unroll
+            for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+                for (int j = 0; j < WTN; ++j) {
+                    mfma_32x32x32_i8(acc[i][j], f0.a[i], f0.b[j]);
+                    if (q < WTM + WTN) load_frag(f1, la, lb, 1, q++);
+                    if (d < C::LPS) {
+                        if (fill) issue_one(st + NST - 1, (st + NST - 1) % NST, d);
+                        ++d;
+                    }
+                }
+            }
+#pragma unroll
+            for (; q < WTM + WTN; ++q) load_frag(f1, la, lb, 1, q);
+#pragma unroll
+            for (; d < C::LPS; ++d)
+                if (fill) issue_one(st + NST - 1, (st + NST - 1) % NST, d);
+            // sub-step 1: MFMAs on f1; read the next stage's sub-step 0 into f0
+            q = 0;
+#pragma unroll
+            for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+                for (int j = 0; j < WTN; ++j) {
+                    mfma_32x32x32_i8(acc[i][j], f1.a[i], f1.b[j]);
+                    // (q advances unconditionally so every register index
+                    // stays a compile-time constant)
+                    if (q < WTM + WTN) {
+                        if (more) load_frag(f0, la_n, lb_n, 0, q);
+                        ++q;
+                    }
+                }
+            }
+#pragma unroll
+            for (; q < WTM + WTN; ++q)
+                if (more) load_frag(f0, la_n, lb_n, 0, q);
+        }
+    } else {
+    #pragma unroll
+        for (int p = 0; p < NST - 1; ++p)
+            if (p < nst) issue(p, p);
+        for (int st = 0; st < nst; ++st) {
+            const int pending = min(st + NST - 2, nst - 1) - st;   // stages issued after st
+            if constexpr (NST >= 4) {
+                if (pending >= 2) wait_vm<2 * C::LPS>();
+                else if (pending == 1) wait_vm<C::LPS>();
+                else wait_vm<0>();
+            } else if constexpr (NST == 3) {
+                if (pending >= 1) wait_vm<C::LPS>();
+                else wait_vm<0>();
+            } else {
+                wait_vm<0>();
+            }
+            __syncthreads();
+            const bool fill = st + NST - 1 < nst;
+            const int fill_st = st + NST - 1, fill_buf = (st + NST - 1) % NST;
+            const int8_t* la = smem + (st % NST) * C::STAGE;
+            const int8_t* lb = la + C::A_BYTES;
+            const int nsub = (half_last && st == nst - 1) ? 2 : C::SUBSTEPS;
+            Frags f[2];
+    #pragma unroll
+            for (int q = 0; q < WTM + WTN; ++q) load_frag(f[0], la, lb, 0, q);
+            int d = 0;   // fill instructions issued so far in this stage
+    #pragma unroll
+            for (int s = 0; s < C::SUBSTEPS; ++s) {
+                if (s >= nsub) break;
+                const Frags& cur = f[s & 1];
+                Frags& nxt = f[(s + 1) & 1];
+                int q = 0;   // next-sub-step fragments issued so far
+    #pragma unroll
+                for (int i = 0; i < WTM; ++i) {
+    #pragma unroll
+                    for (int j = 0; j < WTN; ++j) {
+                        mfma_32x32x32_i8(acc[i][j], cur.a[i], cur.b[j]);
+                        if (s + 1 < C::SUBSTEPS && q < WTM + WTN) load_frag(nxt, la, lb, s + 1, q++);
+                        if (d < C::LPS) {
+                            if (fill) issue_one(fill_st, fill_buf, d);
+                            ++d;
+                        }
+                    }
+                }
+                if (s + 1 < C::SUBSTEPS) {
+                    while (q < WTM + WTN) load_frag(nxt, la, lb, s + 1, q++);
+                }
+            }
+            if (fill) {
+                while (d < C::LPS) issue_one(fill_st, fill_buf, d++);
+            }
         }
     }
+    mfma_drain();
 
-    // ---- integer split-K: last arriver sums the partials in chunk order
+    // ---- integer split-K: the last chunk of a tile to finish adds the others
     if (splitk > 1) {
         const int ntiles = tiles_m * tiles_n;
-        const size_t tile_elems = static_cast<size_t>(T::BM) * T::BN;
+        const size_t tile_elems = static_cast<size_t>(C::BM) * C::BN;
         int32_t* mine = partials + (static_cast<size_t>(split) * ntiles + tile) * tile_elems +
-                        static_cast<size_t>(wave) * T::ACC_PER_WAVE;
+                        static_cast<size_t>(wave) * C::ACC_PER_WAVE;
 #pragma unroll
         for (int i = 0; i < WTM; ++i)
 #pragma unroll
@@ -239,7 +435,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
         // same int32 as P_0 + P_1 + ... + P_{S-1}.  One 32x32 accumulator at
         // a time keeps the register footprint small.
         const int32_t* p0 = partials + static_cast<size_t>(tile) * tile_elems +
-                            static_cast<size_t>(wave) * T::ACC_PER_WAVE;
+                            static_cast<size_t>(wave) * C::ACC_PER_WAVE;
         const size_t cstride = static_cast<size_t>(ntiles) * tile_elems;
 #pragma unroll
         for (int i = 0; i < WTM; ++i) {
@@ -259,24 +455,56 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
         }
     }
 
-    // ---- epilogue, in WTM passes of 64 rows.  Every wave parks one 32-row
-    // slice of its accumulators in LDS (row-major int32, rows padded by 8
-    // words so the two half-waves of a ds_write land in different banks).
-    // Then all 256 threads sweep the 64 x BN slice in float4 chunks along
-    // rows.  Each wave handles one 1 KiB row segment: 16-byte residual loads
-    // and 16-byte output stores, fully coalesced.
-    constexpr int LDR = T::BN + 8;                     // staged row pitch (int32)
+    if constexpr (C::DIRECT_EPI) {
+        // ---- epilogue straight from the accumulators: for a fixed element e,
+        // lanes 0-31 write 32 consecutive floats (128 bytes) of one row and
+        // lanes 32-63 the same of the row 4 below.  No LDS and no barrier.
+        const bool full = (row0 + C::BM <= M) && (col0 + C::BN <= N);
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+            float sxv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = row0 + wm * 32 * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                sxv[e] = sx[min(row, M - 1)];
+            }
+#pragma unroll
+            for (int j = 0; j < WTN; ++j) {
+                const int col = col0 + wn * 32 * WTN + j * 32 + (lane & 31);
+                const float swn = sw[min(col, N - 1)];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = row0 + wm * 32 * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (full || (row < M && col < N)) {
+                        const size_t o = static_cast<size_t>(row) * N + col;
+                        y[o] = residual ? scale_acc_residual(acc[i][j][e], sxv[e], swn, residual[o])
+                                        : scale_acc(acc[i][j][e], sxv[e], swn);
+                    }
+                }
+                sched_fence();
+            }
+        }
+        return;
+    }
+
+    // ---- epilogue, in WTM passes of STAGED_ROWS rows.  Every wave parks one
+    // 32-row slice of its accumulators in LDS (row-major int32, rows padded
+    // by 8 words so the two half-waves of a ds_write land in different
+    // banks).  Then all threads sweep the slice in float4 chunks along rows,
+    // one 16-byte residual load and one 16-byte output store per chunk,
+    // fully coalesced.
+    constexpr int LDR = C::LDR;
     int32_t* stage = reinterpret_cast<int32_t*>(smem);
-    float* s_sx = reinterpret_cast<float*>(smem + 64 * LDR * 4);
-    float* s_sw = s_sx + T::BM;
+    float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
+    float* s_sw = s_sx + C::BM;
     __syncthreads();  // all waves are done reading the operand buffers
-    for (int t = threadIdx.x; t < T::BM; t += THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
-    for (int t = threadIdx.x; t < T::BN; t += THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
+    for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
+    for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
 
     const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                         (reinterpret_cast<uintptr_t>(residual) & 15) == 0;
-    constexpr int C4 = T::BN / 4;                      // float4 chunks per staged row
-    constexpr int ROWS_PER_SWEEP = THREADS / C4;
+    constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
+    constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
     const int c4 = threadIdx.x % C4;
     const int rsub = threadIdx.x / C4;
     const int col = col0 + 4 * c4;
@@ -295,7 +523,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
         }
         __syncthreads();
         const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
-        for (int r = rsub; r < 64; r += ROWS_PER_SWEEP) {
+        for (int r = rsub; r < C::STAGED_ROWS; r += ROWS_PER_SWEEP) {
             // staged row r is tile row (r / 32) * 32 * WTM + pass * 32 + r % 32
             const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
             const int row = row0 + lr;
@@ -334,9 +562,16 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_tiled(
     }
 }
 
-template <int WTM, int WTN>
-hipError_t launch_kind(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {
-    using T = Tile<WTM, WTN>;
+// The configurations, indexed by TileKind.
+using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1>;  // 256x256, 4 waves, 128-byte stages x2
+using Cfg1 = Cfg<2, 4, 4, 2, 64, 4, 1>;   // 256x256, 8 waves, 64-byte stages x4
+using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per CU
+using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU
+using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1>;  // 256x256, 8 waves, 128-byte stages x2
+using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true>;  // as 4, epilogue stored from the accumulators
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {
     const int64_t ntiles = p.tiles_m * p.tiles_n;
     const int KB = static_cast<int>(a.K >> 6);
     const int kb_per_split = (KB + p.splitk - 1) / p.splitk;
@@ -348,14 +583,28 @@ hipError_t launch_kind(const GemmArgs& a, const GemmPlan& p, void* workspace, hi
         partials = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cbytes);
     }
     const unsigned nblocks = static_cast<unsigned>(ntiles * p.splitk);
-    hipLaunchKernelGGL((gemm_tiled<WTM, WTN>), dim3(nblocks), dim3(THREADS), 0, stream, a.xq, a.sx,
-                       a.w, a.sw, a.residual, a.y, static_cast<int>(a.M), static_cast<int>(a.N),
+    hipLaunchKernelGGL((gemm_tiled<C>), dim3(nblocks), dim3(C::THREADS), 0, stream, a.xq, a.sx, a.w,
+                       a.sw, a.residual, a.y, static_cast<int>(a.M), static_cast<int>(a.N),
                        static_cast<int>(a.K), static_cast<int>(p.tiles_m),
                        static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, counters,
                        partials);
-    (void)sizeof(T);
     return hipGetLastError();
 }
+
+struct KindInfo {
+    int bm, bn;
+    int per_cu;     // workgroups resident per CU
+    double weight;  // relative per-CU throughput of the shape
+};
+// Same order as TileKind and the Cfg list.
+const KindInfo kKinds[TILE_KINDS] = {
+    {Cfg0::BM, Cfg0::BN, Cfg0::OCC, 0.95},
+    {Cfg1::BM, Cfg1::BN, Cfg1::OCC, 0.93},
+    {Cfg2::BM, Cfg2::BN, Cfg2::OCC, 0.85},
+    {Cfg3::BM, Cfg3::BN, Cfg3::OCC, 0.70},
+    {Cfg4::BM, Cfg4::BN, Cfg4::OCC, 1.00},
+    {Cfg5::BM, Cfg5::BN, Cfg5::OCC, 0.97},
+};
 
 int tile_override = -1;
 
@@ -365,39 +614,31 @@ void set_tile_override(int kind) { tile_override = kind; }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
     (void)K;
-    struct Cand {
-        TileKind kind;
-        int bm, bn;
-        double weight;  // relative per-CU throughput of the tile shape
-    };
-    static const Cand cands[] = {
-        {TILE_256x256, 256, 256, 1.00},
-        {TILE_256x128, 256, 128, 0.90},
-        {TILE_128x128, 128, 128, 0.75},
-    };
     const int ncu = 256;
     int best = 0;
     double best_score = -1.0;
-    for (int c = 0; c < 3; ++c) {
-        const int64_t tm = (M + cands[c].bm - 1) / cands[c].bm;
-        const int64_t tn = (N + cands[c].bn - 1) / cands[c].bn;
+    for (int c = 0; c < TILE_KINDS; ++c) {
+        const KindInfo& k = kKinds[c];
+        const int64_t tm = (M + k.bm - 1) / k.bm;
+        const int64_t tn = (N + k.bn - 1) / k.bn;
         const int64_t blocks = tm * tn * splitk;
-        const int64_t rounds = (blocks + ncu - 1) / ncu;
+        const int64_t slots = static_cast<int64_t>(ncu) * k.per_cu;
+        const int64_t rounds = (blocks + slots - 1) / slots;
         // useful work over the slots the rounds occupy, times the shape's speed
         const double useful = static_cast<double>(M) * static_cast<double>(N) /
-                              (static_cast<double>(tm * cands[c].bm) * static_cast<double>(tn * cands[c].bn));
-        const double fill = static_cast<double>(blocks) / static_cast<double>(rounds * ncu);
-        const double score = useful * fill * cands[c].weight;
+                              (static_cast<double>(tm * k.bm) * static_cast<double>(tn * k.bn));
+        const double fill = static_cast<double>(blocks) / static_cast<double>(rounds * slots);
+        const double score = useful * fill * k.weight;
         if (score > best_score + 1e-9) {
             best_score = score;
             best = c;
         }
     }
-    if (tile_override >= 0 && tile_override < 3) best = tile_override;
+    if (tile_override >= 0 && tile_override < TILE_KINDS) best = tile_override;
     GemmPlan p;
-    p.kind = cands[best].kind;
-    p.bm = cands[best].bm;
-    p.bn = cands[best].bn;
+    p.kind = static_cast<TileKind>(best);
+    p.bm = kKinds[best].bm;
+    p.bn = kKinds[best].bn;
     p.tiles_m = (M + p.bm - 1) / p.bm;
     p.tiles_n = (N + p.bn - 1) / p.bn;
     p.splitk = splitk;
@@ -415,9 +656,13 @@ size_t gemm_workspace_bytes(const GemmPlan& p) {
 hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,
                              hipStream_t stream) {
     switch (p.kind) {
-        case TILE_256x256: return launch_kind<4, 4>(a, p, workspace, stream);
-        case TILE_256x128: return launch_kind<4, 2>(a, p, workspace, stream);
-        case TILE_128x128: return launch_kind<2, 2>(a, p, workspace, stream);
+        case 0: return launch_cfg<Cfg0>(a, p, workspace, stream);
+        case 1: return launch_cfg<Cfg1>(a, p, workspace, stream);
+        case 2: return launch_cfg<Cfg2>(a, p, workspace, stream);
+        case 3: return launch_cfg<Cfg3>(a, p, workspace, stream);
+        case 4: return launch_cfg<Cfg4>(a, p, workspace, stream);
+        case 5: return launch_cfg<Cfg5>(a, p, workspace, stream);
+        default: break;
     }
     return hipErrorInvalidValue;
 }

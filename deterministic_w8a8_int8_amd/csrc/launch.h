@@ -36,7 +36,12 @@ struct GemmArgs {
 
 // Tiled MFMA GEMM.  Which tile shape runs depends only on (M, N, K, splitk);
 // the workspace query and the launch use the same choice.
-enum TileKind { TILE_256x256 = 0, TILE_256x128 = 1, TILE_128x128 = 2 };
+// Tile configurations of the tiled kernel (see gemm_tiled.hip):
+//   0: 256x256, 4 waves, 128-byte K stages x2      1: 256x256, 8 waves, 64-byte x4
+//   2: 256x128, 4 waves, 2 workgroups per CU        3: 128x128, 2 workgroups per CU
+//   4: 256x256, 8 waves, 128-byte K stages x2
+//   5: as 4, epilogue written straight from the accumulators
+enum TileKind { TILE_KIND_0 = 0, TILE_KIND_1, TILE_KIND_2, TILE_KIND_3, TILE_KIND_4, TILE_KIND_5, TILE_KINDS };
 
 struct GemmPlan {
     TileKind kind;
@@ -76,5 +81,10 @@ struct SkinnyArgs {
 };
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
+
+// Diagnostic MFMA-only kernel (mfma_ceiling.hip).
+int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters);
+hipError_t launch_mfma_ceiling(int kind, int64_t blocks, int64_t iters, int32_t* sink,
+                               hipStream_t stream);
 
 }  // namespace w8a8

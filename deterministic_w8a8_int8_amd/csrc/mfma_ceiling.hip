@@ -1,0 +1,105 @@
+// Diagnostic: sustained int8 MFMA throughput with no memory traffic.
+//
+// The int8 matrix cores of MI355X do not sustain their nominal rate on
+// every operand stream.  With zero or constant operands they run near the
+// nominal 5 POP/s.  With operands that change every instruction and whose
+// bits toggle, the sustained rate is markedly lower.  This kernel measures
+// that ceiling, so a GEMM's throughput can be judged against what the
+// matrix cores deliver on comparable data as well as against the nominal
+// peak.
+//
+// Each wave keeps eight 32x32 int32 accumulators and cycles through four
+// register-resident operand sets (A in 4 fragments, B in 2), so every
+// v_mfma_i32_32x32x32_i8 sees new operands and no memory is touched inside
+// the loop.  Operand kinds:
+//   0  A and B uniform on [-128, 127]
+//   1  A shaped like per-token-quantised activations (mostly 0 and +-1, a few
+//      large outlier values), B uniform
+// The operands come from an integer hash of the thread and slot numbers.
+#include "device_common.h"
+#include "launch.h"
+
+namespace w8a8 {
+
+namespace {
+
+constexpr int CEIL_THREADS = 512;
+
+__device__ __forceinline__ void mfma_acc(i32x16& c, const i32x4& a, const i32x4& b) {
+    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
+}
+
+__device__ __forceinline__ int activation_like_byte(uint32_t h) {
+    const uint32_t r = h & 255u;
+    const int v = r < 180 ? 0 : r < 230 ? 1 : r < 250 ? 2 : 20 + static_cast<int>((h >> 8) % 100u);
+    return ((h >> 20) & 1u) ? -v : v;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sink, int64_t iters) {
+    const uint32_t t = threadIdx.x + blockIdx.x * CEIL_THREADS;
+    i32x4 a[4][4], b[4][2];
+    for (int s = 0; s < 4; ++s) {
+        for (int i = 0; i < 4; ++i) {
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w = 0;
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t h = mix32(t * 4096u + s * 256u + i * 16u + e * 4u + q);
+                    const int v = KIND == 0 ? static_cast<int>(h & 255u) - 128 : activation_like_byte(h);
+                    w |= (static_cast<uint32_t>(v) & 255u) << (8 * q);
+                }
+                a[s][i][e] = static_cast<int32_t>(w);
+            }
+        }
+        for (int j = 0; j < 2; ++j)
+            for (int e = 0; e < 4; ++e) b[s][j][e] = static_cast<int32_t>(mix32(t * 4096u + 2048u + s * 64u + j * 8u + e));
+    }
+    i32x16 c[4][2];
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 2; ++j)
+            for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) mfma_acc(c[i][j], a[s][i], b[s][j]);
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    int32_t x = 0;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 2; ++j)
+            for (int e = 0; e < 16; ++e) x ^= c[i][j][e];
+    // keeps the products alive; the sink is written only for this one value
+    if (x == 0x7a5c3e1f) sink[0] = x;
+}
+
+}  // namespace
+
+int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters) {
+    // per iteration and wave: 32 MFMAs of 32*32*32 multiply-adds (2 ops each)
+    return blocks * (CEIL_THREADS / 64) * iters * 32 * (2LL * 32 * 32 * 32);
+}
+
+hipError_t launch_mfma_ceiling(int kind, int64_t blocks, int64_t iters, int32_t* sink,
+                               hipStream_t stream) {
+    if (kind == 0)
+        hipLaunchKernelGGL(mfma_ceiling_kernel<0>, dim3(static_cast<unsigned>(blocks)),
+                           dim3(CEIL_THREADS), 0, stream, sink, iters);
+    else
+        hipLaunchKernelGGL(mfma_ceiling_kernel<1>, dim3(static_cast<unsigned>(blocks)),
+                           dim3(CEIL_THREADS), 0, stream, sink, iters);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

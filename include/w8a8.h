@@ -71,12 +71,30 @@ const char* w8a8_status_string(int status);
 /* Version of this ABI: major*10000 + minor*100 + patch (host). */
 int w8a8_abi_version(void);
 
-/* Tuning and test hook (host, process-wide): force the tile shape of the
- * tiled GEMM for later calls.  -1 = automatic (the default), 0 = 256x256,
- * 1 = 256x128, 2 = 128x128.  It never changes a result bit, only speed.  It
- * also changes the split-K workspace size, so query the size again after
- * changing it.  Returns W8A8_ERR_INVALID_ARG for other values. */
+/* Tuning and test hook (host, process-wide): force the tile configuration of
+ * the tiled GEMM for later calls.  -1 = automatic (the default); 0..5 pick
+ * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
+ * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
+ * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
+ * stages, 5: as 4 with the epilogue stored straight from the accumulators).  It never changes a result bit, only speed.  It also changes the
+ * split-K workspace size, so query the size again after changing it.
+ * Returns W8A8_ERR_INVALID_ARG for other values. */
 int w8a8_set_tile_override(int kind);
+
+/*
+ * Diagnostic (not part of the layer): launch an MFMA-only kernel that runs
+ * v_mfma_i32_32x32x32_i8 on register-resident operands, with no memory
+ * traffic, so the caller can time the throughput the int8 matrix cores
+ * sustain on a given kind of operand data.  operand_kind 0: A and B uniform
+ * int8; 1: A shaped like per-token-quantised activations (mostly 0 and +-1),
+ * B uniform.  blocks x 512 threads run `iters` iterations.  *ops (host,
+ * nullable) receives the number of int8 operations (2 per multiply-add)
+ * launched.  sink: device int32, written only in the impossible case that
+ * an xor of all accumulators equals a fixed constant (it keeps the work
+ * alive).  Asynchronous on `stream`.
+ */
+int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
+                            int64_t* ops, void* stream);
 
 /*
  * w8a8_quantize_act -- per-token int8 quantisation after a per-channel

@@ -109,5 +109,8 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 65, p, nul, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 0, p, 4, p, nul, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 0, p, nul, S) == B.W8A8_OK
-    assert lib.w8a8_set_tile_override(5) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_set_tile_override(99) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_set_tile_override(-2) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_probe_mfma_ceiling(2, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_probe_mfma_ceiling(0, 0, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
     del keep
