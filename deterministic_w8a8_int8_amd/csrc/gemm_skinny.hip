@@ -14,15 +14,22 @@
 // Design (HBM-bound: each weight byte is used by only M <= 64 rows):
 //   - a wave owns 16 weight rows (output columns) and all M activation rows,
 //     as R = ceil(M/16) v_mfma_i32_16x16x64_i8 accumulators;
-//   - weight fragments stream straight from HBM into VGPRs, 16 bytes per lane,
-//     U = 8 K-steps (512 bytes of every row, 4 full cache lines) per batch,
-//     with the next batch in flight while the current one multiplies.  No LDS
-//     and no barrier is involved;
-//   - activation fragments are small and shared by every wave.  They come
-//     through L1/L2; lanes whose row is >= M feed zeros and issue no load;
+//   - weight fragments stream straight from HBM into VGPRs, 16 bytes per
+//     lane.  U K-steps of 64 bytes are one batch: every row of the wave gets
+//     U*64 contiguous bytes.  The activation fragments of the same K-steps are
+//     loaded in the same batch, and the next batch is in flight while the
+//     current one multiplies.  No LDS, no barrier;
+//   - lanes whose activation row is >= M feed zeros and issue no load; for
+//     M <= 16 with M*(K+16) <= 40 KiB the activation rows are first staged in
+//     LDS, so the weight stream is the only vector-memory traffic;
 //   - as in the tiled kernel, any lane -> k assignment that A and B share
 //     gives the same exact sum.  The 16x16 result tile puts row
 //     4*(lane/16) + e and column lane % 16 in lane `lane`, element e;
+//   - K-parallel mode (KSPLIT > 1, for outputs too narrow to fill the GPU,
+//     such as the candidate read-out): KSPLIT waves of one workgroup share a
+//     16-column tile, each takes a contiguous slice of the K-steps, and the
+//     int32 partials are added through LDS.  Integer addition is exact, so
+//     the slice count never changes a bit;
 //   - gathered mode reads weight row gather[j] for output column j, bounds-
 //     checked against V: an id outside [0, V) reads row 0 and writes a quiet
 //     NaN, then ORs bit 0 into err_flag.  Owner mode writes only column j of
@@ -34,20 +41,19 @@ namespace w8a8 {
 
 namespace {
 
-constexpr int STHREADS = 256;   // 4 waves, 16 columns each
-constexpr int U = 8;            // K-steps of 64 bytes per streamed batch
-
-template <int R>
-__global__ __launch_bounds__(STHREADS) void gemm_skinny(
+// R: 16-row activation groups; U: K-steps per streamed batch;
+// KSPLIT: waves sharing one column tile (1 = four independent column tiles per workgroup).
+// ALDS: activation rows staged in LDS (R == 1, M * K small enough).
+template <int R, int U, int KSPLIT, bool ALDS>
+__global__ __launch_bounds__(KSPLIT > 1 ? 64 * KSPLIT : 256) void gemm_skinny(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* residual, float* y, int64_t M, int64_t N, int64_t K,
     int64_t ldy, const int32_t* __restrict__ gather, int64_t V, int64_t owner_c,
     int32_t* __restrict__ err_flag) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 16;
-    if (n0 >= N) return;
-
+    const int64_t n0 = KSPLIT > 1 ? static_cast<int64_t>(blockIdx.x) * 16
+                                  : (static_cast<int64_t>(blockIdx.x) * 4 + wave) * 16;
     // this lane's weight row
     const int64_t n = min(n0 + (lane & 15), N - 1);
     int64_t wrow = n;
@@ -68,49 +74,103 @@ __global__ __launch_bounds__(STHREADS) void gemm_skinny(
         ap[g] = A + (arow_ok[g] ? m : 0) * K + kq;
     }
 
+    // this wave's K-steps
+    const int64_t steps = K >> 6;
+    int64_t s0 = 0, s1 = steps;
+    if (KSPLIT > 1) {
+        const int64_t per = (steps + KSPLIT - 1) / KSPLIT;
+        s0 = min(static_cast<int64_t>(wave) * per, steps);
+        s1 = min(s0 + per, steps);
+    }
+
+    // Activation rows in LDS: loaded once per workgroup (16-byte pieces,
+    // coalesced), row pitch K + 16 bytes so the active lanes of a fragment
+    // read hit different banks.
+    extern __shared__ __attribute__((aligned(16))) int8_t a_lds[];
+    const int64_t apitch = K + 16;
+    if constexpr (ALDS) {
+        const int64_t pieces = M * (K >> 4);
+        for (int64_t p = threadIdx.x; p < pieces; p += blockDim.x) {
+            const int64_t m = p / (K >> 4), c = p % (K >> 4);
+            *reinterpret_cast<i32x4*>(a_lds + m * apitch + c * 16) =
+                *reinterpret_cast<const i32x4*>(A + m * K + c * 16);
+        }
+        __syncthreads();
+    }
+    // Only after every wave has done its share of the staging may a wave
+    // without columns leave (uniform across the workgroup in K-parallel mode).
+    if (n0 >= N) return;
+    const int8_t* al = a_lds + (arow_ok[0] ? static_cast<int64_t>(lane & 15) : 0) * apitch + kq;
+
     i32x4 acc[R];
 #pragma unroll
     for (int g = 0; g < R; ++g) acc[g] = i32x4{0, 0, 0, 0};
 
-    const int64_t steps = K >> 6;
-    const int64_t batches = steps / U;
-    i32x4 wcur[U];
-    if (batches > 0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) wcur[u] = *reinterpret_cast<const i32x4*>(wp + u * 64);
-    }
-    for (int64_t b = 0; b < batches; ++b) {
-        i32x4 wnext[U];
-        const bool more = (b + 1) < batches;
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                wnext[u] = *reinterpret_cast<const i32x4*>(wp + ((b + 1) * U + u) * 64);
+    auto a_frag = [&](int g, int64_t s) -> i32x4 {
+        if constexpr (ALDS) {
+            return arow_ok[0] ? *reinterpret_cast<const i32x4*>(al + s * 64) : i32x4{0, 0, 0, 0};
+        } else {
+            return arow_ok[g] ? *reinterpret_cast<const i32x4*>(ap[g] + s * 64) : i32x4{0, 0, 0, 0};
         }
+    };
+    struct Batch {
+        i32x4 w[U];
+        i32x4 a[ALDS ? 1 : R][ALDS ? 1 : U];
+    };
+    auto load = [&](Batch& bt, int64_t s) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t koff = (b * U + u) * 64;
+        for (int u = 0; u < U; ++u) bt.w[u] = *reinterpret_cast<const i32x4*>(wp + (s + u) * 64);
+        if constexpr (!ALDS) {
+#pragma unroll
+            for (int g = 0; g < R; ++g)
+#pragma unroll
+                for (int u = 0; u < U; ++u) bt.a[g][u] = a_frag(g, s + u);
+        }
+    };
+    auto multiply = [&](const Batch& bt, int64_t s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int g = 0; g < R; ++g) {
-                const i32x4 a = arow_ok[g] ? *reinterpret_cast<const i32x4*>(ap[g] + koff)
-                                           : i32x4{0, 0, 0, 0};
-                acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wcur[u], acc[g], 0, 0, 0);
+                const i32x4 a = ALDS ? a_frag(g, s + u) : bt.a[ALDS ? 0 : g][ALDS ? 0 : u];
+                acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bt.w[u], acc[g], 0, 0, 0);
             }
-        }
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) wcur[u] = wnext[u];
-        }
+    };
+
+    const int64_t batches = (s1 - s0) / U;
+    Batch cur, nxt;
+    if (batches > 0) load(cur, s0);
+    for (int64_t b = 0; b < batches; ++b) {
+        const bool more = (b + 1) < batches;
+        if (more) load(nxt, s0 + (b + 1) * U);
+        multiply(cur, s0 + b * U);
+        if (more) cur = nxt;
     }
-    // remaining K-steps (K/64 not a multiple of U)
-    for (int64_t s = batches * U; s < steps; ++s) {
+    // remaining K-steps of the slice
+    for (int64_t s = s0 + batches * U; s < s1; ++s) {
         const i32x4 wv = *reinterpret_cast<const i32x4*>(wp + s * 64);
 #pragma unroll
-        for (int g = 0; g < R; ++g) {
-            const i32x4 a = arow_ok[g] ? *reinterpret_cast<const i32x4*>(ap[g] + s * 64)
-                                       : i32x4{0, 0, 0, 0};
-            acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv, acc[g], 0, 0, 0);
-        }
+        for (int g = 0; g < R; ++g)
+            acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_frag(g, s), wv, acc[g], 0, 0, 0);
+    }
+
+    if constexpr (KSPLIT > 1) {
+        // add the slices' exact int32 partials through LDS; wave 0 finishes
+        __shared__ int32_t red[KSPLIT][R * 4][64];
+#pragma unroll
+        for (int g = 0; g < R; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wave][g * 4 + e][lane] = acc[g][e];
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int g = 0; g < R; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                int32_t t = 0;
+                for (int w = 0; w < KSPLIT; ++w) t += red[w][g * 4 + e][lane];
+                acc[g][e] = t;
+            }
     }
 
     // epilogue: lane holds rows 16g + 4*(lane/16) + e of column n0 + lane%16
@@ -143,23 +203,46 @@ __global__ __launch_bounds__(STHREADS) void gemm_skinny(
     if (flagged && err_flag) atomicOr(err_flag, 1);
 }
 
-template <int R>
+template <int R, int U, int KSPLIT, bool ALDS>
 hipError_t launch_r(const SkinnyArgs& a, hipStream_t stream) {
-    const int64_t blocks = (a.N + 63) / 64;
-    hipLaunchKernelGGL(gemm_skinny<R>, dim3(static_cast<unsigned>(blocks)), dim3(STHREADS), 0,
-                       stream, a.xq, a.sx, a.w, a.sw, a.residual, a.y, a.M, a.N, a.K, a.ldy,
-                       a.gather, a.V, a.owner_c, a.err_flag);
+    const int64_t tiles = (a.N + 15) / 16;
+    const int64_t blocks = KSPLIT > 1 ? tiles : (tiles + 3) / 4;
+    const int threads = KSPLIT > 1 ? 64 * KSPLIT : 256;
+    const size_t lds = ALDS ? static_cast<size_t>(a.M * (a.K + 16)) : 0;
+    hipLaunchKernelGGL((gemm_skinny<R, U, KSPLIT, ALDS>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(threads), lds, stream, a.xq, a.sx, a.w, a.sw, a.residual, a.y, a.M, a.N,
+                       a.K, a.ldy, a.gather, a.V, a.owner_c, a.err_flag);
     return hipGetLastError();
+}
+
+// Activation rows go to LDS when they fit comfortably (R == 1 only).
+constexpr int64_t kSkinnyLdsBytes = 40 * 1024;
+
+template <int R, int U, bool ALDS>
+hipError_t launch_rk(const SkinnyArgs& a, hipStream_t stream) {
+    // Narrow outputs cannot fill 256 CUs with one wave per 16 columns: split K
+    // over up to 16 waves per column tile instead.
+    const int64_t tiles = (a.N + 15) / 16;
+    const int64_t steps = a.K >> 6;
+    if constexpr (R == 1) {
+        // 16 waves per workgroup leave 128 VGPRs per lane: use 4-step batches
+        if (tiles < 256 && steps >= 64) return launch_r<1, 4, 16, ALDS>(a, stream);
+    }
+    if (tiles < 1024 && steps >= 32) return launch_r<R, U, 4, ALDS>(a, stream);
+    return launch_r<R, U, 1, ALDS>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
-    if (a.M <= 16) return launch_r<1>(a, stream);
-    if (a.M <= 32) return launch_r<2>(a, stream);
-    if (a.M <= 48) return launch_r<3>(a, stream);
-    return launch_r<4>(a, stream);
+    if (a.M <= 16) {
+        if (a.M * (a.K + 16) <= kSkinnyLdsBytes) return launch_rk<1, 8, true>(a, stream);
+        return launch_rk<1, 8, false>(a, stream);
+    }
+    if (a.M <= 32) return launch_rk<2, 4, false>(a, stream);
+    if (a.M <= 48) return launch_rk<3, 4, false>(a, stream);
+    return launch_rk<4, 4, false>(a, stream);
 }
 
 }  // namespace w8a8

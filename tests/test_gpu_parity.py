@@ -93,6 +93,8 @@ def _gemm_case(M, N, K, seed, residual):
 
 SHAPES = [
     (1, 7, 64), (3, 256, 320), (16, 256, 256), (64, 130, 192),      # skinny kernel
+    (3, 300, 2048), (40, 500, 2560), (5, 40, 4096), (16, 1000, 5120),  # skinny, K split over waves
+    (3, 20, 1024),   # two column tiles: half of the workgroup has no columns (LDS staging regression)
     (65, 100, 64), (200, 257, 192), (300, 520, 1024), (513, 264, 320), (256, 256, 256),
 ]
 
