@@ -10,16 +10,32 @@
 //   q  = clamp(rne(fl(x' / sx)), -127, 127), or 0 when sx == 0
 //
 // Design (HBM-bound scan, 4 B read + 1 B written per element):
-//   - one 256-thread workgroup per output row; thread t holds float4 number
-//     t + 256*i of the row in registers, so the row is read from HBM once
-//     and every wave-level load is 1 KiB contiguous;
-//   - x' is kept in registers between the max and the quantisation;
-//   - the row maximum is a wave64 shuffle reduction, then four partial
+//   - a workgroup of T = 256 or 512 threads handles one row; thread t holds
+//     float4 number t + T*i of the row in registers, so each row is read from
+//     HBM once and every wave-level load is 1 KiB contiguous;
+//   - exact results without a true division per element.  Two correctly
+//     rounded divisions per element would cost as much as the memory
+//     traffic, so the kernel works with reciprocals and proves, per element,
+//     that the cheap value decides the same bits:
+//       * r = rcp(s) (|error| <= 1 ulp) is computed once per column of the
+//         workgroup's row.  x*r is within 2^-22
+//         (relative) of fl(x/s).  The row maximum is found on these
+//         approximations.  Because fl() is monotone, the exact maximum
+//         fl(|x_k|/s_k) is reached by an element whose approximation lies
+//         within 2^-19 of the approximate maximum.  Only those few
+//         candidates are divided exactly;
+//       * with sx = fl(a/127) (a true division, once per row) and inv =
+//         rcp(sx), t' = (x*r)*inv is within 2^-14 of t = fl(fl(x/s)/sx)
+//         whenever |t| <= 128.  If t' is more than 2^-12 away from every
+//         half-integer, rne(t') = rne(t).  Otherwise (about 5 in 10^4
+//         elements) both true divisions are done;
+//       * rows whose approximate maximum is below 2^-96, or whose smoothing
+//         values lie outside [2^-120, 2^120], where subnormal intermediates
+//         void the relative error bounds, take the exact path throughout;
+//   - the row maximum is a wave64 shuffle reduction, then per-wave partial
 //     maxima through LDS (max is exact, so order does not matter);
-//   - rows longer than the register budget (K > 32768) take a two-pass
-//     variant that reads x twice, recomputing the identical quotients;
-//   - both divisions are true IEEE divisions (hipcc's default expansion is
-//     correctly rounded), and rne is v_rndne_f32.
+//   - rows longer than the register budget (K > 32768) take an exact
+//     two-pass variant that reads x twice.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,40 +43,66 @@ namespace w8a8 {
 
 namespace {
 
-constexpr int QTHREADS = 256;
+constexpr int QTHREADS = 256;   // workgroup of the exact two-pass kernel
 
-__device__ __forceinline__ int8_t quantize_one(float v, float scale) {
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// Exact quantisation of one smoothed value (both true divisions done).
+__device__ __forceinline__ int8_t quantize_exact(float x, float s, float scale) {
     if (scale == 0.0f) return 0;
-    const float t = v / scale;
-    float r = rintf(t);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    const float t = (x / s) / scale;
+    const float r = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
     return static_cast<int8_t>(static_cast<int>(r));
 }
 
-__device__ __forceinline__ uint32_t pack4(float4 v, float scale) {
-    const uint32_t b0 = static_cast<uint8_t>(quantize_one(v.x, scale));
-    const uint32_t b1 = static_cast<uint8_t>(quantize_one(v.y, scale));
-    const uint32_t b2 = static_cast<uint8_t>(quantize_one(v.z, scale));
-    const uint32_t b3 = static_cast<uint8_t>(quantize_one(v.w, scale));
-    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+// Fast quantisation with the proof described above; falls back to the exact
+// divisions when the approximate quotient is near a rounding boundary.
+__device__ __forceinline__ int8_t quantize_fast(float x, float r, const float4* s4, int j, int c,
+                                                float scale, float inv) {
+    const float t = (x * r) * inv;
+    const float d = fabsf((t - floorf(t)) - 0.5f);
+    float q;
+    if (d > 0x1p-12f) {
+        q = rintf(t);
+    } else {
+        const float s = reinterpret_cast<const float*>(s4)[4 * j + c];
+        q = rintf((x / s) / scale);
+    }
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return static_cast<int8_t>(static_cast<int>(q));
 }
 
-__device__ __forceinline__ float4 smooth4(float4 a, float4 s) {
-    return make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w);
-}
+__device__ __forceinline__ float4 f4(float v) { return make_float4(v, v, v, v); }
 
 __device__ __forceinline__ float absmax4(float m, float4 v) {
     return fmaxf(fmaxf(fmaxf(m, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
 }
 
-// Block-wide maximum of one float per thread (4 waves).
+// Block-wide maximum of one float per thread (NW waves).  `red` must not be
+// reused until every thread has read the result: callers alternate buffers.
+template <int NW>
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    return v;
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
+    return m;
+}
+
+// Block-wide OR of a flag.
+template <int NW>
+__device__ __forceinline__ bool block_any(bool v, int* red) {
+    const bool w = __any(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = w ? 1 : 0;
+    __syncthreads();
+    int o = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) o |= red[i];
+    return o != 0;
 }
 
 // Resolve the source row; an index outside [0, x_rows) marks the row invalid.
@@ -76,46 +118,117 @@ __device__ __forceinline__ bool source_row(const int32_t* row_idx, int64_t m, in
     return ok;
 }
 
-// NV float4 per thread held in registers: K <= NV * 4 * 256.
-template <int NV>
-__global__ __launch_bounds__(QTHREADS) void quantize_rows_reg(
+__device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d) {
+    return static_cast<uint32_t>(static_cast<uint8_t>(a)) |
+           (static_cast<uint32_t>(static_cast<uint8_t>(b)) << 8) |
+           (static_cast<uint32_t>(static_cast<uint8_t>(c)) << 16) |
+           (static_cast<uint32_t>(static_cast<uint8_t>(d)) << 24);
+}
+
+// NV float4 per thread held in registers: K <= NV * 4 * T; ROWS rows per
+// workgroup of T threads.
+template <int NV, int T, int ROWS>
+__global__ __launch_bounds__(T) void quantize_rows_reg(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
-    const float* __restrict__ smooth, int64_t K, int8_t* __restrict__ xq, float* __restrict__ sx) {
-    __shared__ float red[4];
-    const int64_t m = blockIdx.x;
-    int64_t src;
-    const bool ok = source_row(row_idx, m, x_rows, &src);
-    const float4* xr = reinterpret_cast<const float4*>(x + src * ldx);
+    const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
+    float* __restrict__ sx) {
+    constexpr int NW = T / 64;
+    __shared__ float redf[4][NW];
+    __shared__ int redi[NW];
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
     const int K4 = static_cast<int>(K >> 2);
     const int t = threadIdx.x;
 
-    float4 v[NV];
-    float amax = 0.0f;
+    // per-column reciprocals of the smoothing values, shared by the block's
+    // rows (the smoothing values themselves are reloaded on the rare exact
+    // paths)
+    float4 rv[NV];
+    bool odd_s = false;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int j = t + i * QTHREADS;
-        if (j < K4) {
-            v[i] = smooth4(xr[j], s4[j]);
-            amax = absmax4(amax, v[i]);
-        } else {
-            v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        const int j = t + i * T;
+        const float4 sv = j < K4 ? s4[j] : f4(1.0f);
+        rv[i] = make_float4(fast_rcp(sv.x), fast_rcp(sv.y), fast_rcp(sv.z), fast_rcp(sv.w));
+        const float lo = fminf(fminf(sv.x, sv.y), fminf(sv.z, sv.w));
+        const float hi = fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w));
+        odd_s |= !(lo >= 0x1p-120f && hi <= 0x1p120f);
     }
-    amax = block_max(amax, red);
-    const float scale = ok ? amax / 127.0f : 0.0f;
-    if (t == 0) sx[m] = ok ? scale : quiet_nan();
+    const bool odd_cols = block_any<NW>(odd_s, redi);
 
-    uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+    for (int rr = 0; rr < ROWS; ++rr) {
+        const int64_t m = m0 + rr;
+        if (m >= M) break;   // uniform across the block
+        int64_t src;
+        const bool ok = source_row(row_idx, m, x_rows, &src);
+        const float4* xr = reinterpret_cast<const float4*>(x + src * ldx);
+
+        float4 xv[NV];
+        float amax_a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int j = t + i * QTHREADS;
-        if (j < K4) qr[j] = pack4(v[i], scale);
+        for (int i = 0; i < NV; ++i) {
+            const int j = t + i * T;
+            xv[i] = j < K4 ? xr[j] : f4(0.0f);
+            const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y, xv[i].z * rv[i].z,
+                                          xv[i].w * rv[i].w);
+            amax_a = absmax4(amax_a, ap);
+        }
+        float* red0 = redf[(2 * rr) & 3];
+        float* red1 = redf[(2 * rr + 1) & 3];
+        amax_a = block_max<NW>(amax_a, red0);
+        const bool exact_row = odd_cols || !(amax_a >= 0x1p-96f);
+
+        // exact maximum: true divisions for the candidates only (or every
+        // element on an exact row)
+        const float thresh = amax_a * (1.0f - 0x1p-19f);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int j = t + i * T;
+            if (j >= K4) continue;
+            const float xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            const float rs[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+            bool any = exact_row;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
+            if (any) {
+                const float4 sv = s4[j];
+                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (exact_row || fabsf(xs[c] * rs[c]) >= thresh) amax = fmaxf(amax, fabsf(xs[c] / ss[c]));
+            }
+        }
+        amax = block_max<NW>(amax, red1);
+        const float scale = ok ? amax / 127.0f : 0.0f;
+        if (t == 0) sx[m] = ok ? scale : quiet_nan();
+        const float inv = fast_rcp(scale);
+
+        uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int j = t + i * T;
+            if (j >= K4) continue;
+            uint32_t packed = 0;
+            if (scale != 0.0f) {
+                if (exact_row) {
+                    const float4 sv = s4[j];
+                    packed = pack4(quantize_exact(xv[i].x, sv.x, scale), quantize_exact(xv[i].y, sv.y, scale),
+                                   quantize_exact(xv[i].z, sv.z, scale), quantize_exact(xv[i].w, sv.w, scale));
+                } else {
+                    packed = pack4(quantize_fast(xv[i].x, rv[i].x, s4, j, 0, scale, inv),
+                                   quantize_fast(xv[i].y, rv[i].y, s4, j, 1, scale, inv),
+                                   quantize_fast(xv[i].z, rv[i].z, s4, j, 2, scale, inv),
+                                   quantize_fast(xv[i].w, rv[i].w, s4, j, 3, scale, inv));
+                }
+            }
+            qr[j] = packed;
+        }
     }
 }
 
-// Any K: the row is read twice (the second read usually hits L2); the
-// quotients are recomputed bit-identically.
+// Any K: the row is read twice (the second read usually hits L2) and every
+// element takes the exact divisions.
 __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t K, int8_t* __restrict__ xq, float* __restrict__ sx) {
@@ -128,19 +241,28 @@ __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     const int64_t K4 = K >> 2;
 
     float amax = 0.0f;
-    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) amax = absmax4(amax, smooth4(xr[j], s4[j]));
-    amax = block_max(amax, red);
+    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
+        const float4 a = xr[j], s = s4[j];
+        amax = absmax4(amax, make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w));
+    }
+    amax = block_max<QTHREADS / 64>(amax, red);
     const float scale = ok ? amax / 127.0f : 0.0f;
     if (threadIdx.x == 0) sx[m] = ok ? scale : quiet_nan();
 
     uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
-    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) qr[j] = pack4(smooth4(xr[j], s4[j]), scale);
+    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
+        const float4 a = xr[j], s = s4[j];
+        qr[j] = pack4(quantize_exact(a.x, s.x, scale), quantize_exact(a.y, s.y, scale),
+                      quantize_exact(a.z, s.z, scale), quantize_exact(a.w, s.w, scale));
+    }
 }
 
-template <int NV>
+template <int NV, int T>
 hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(quantize_rows_reg<NV>, dim3(static_cast<unsigned>(a.M)), dim3(QTHREADS), 0,
-                       stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, a.xq, a.sx);
+    // One row per workgroup: measured faster than sharing the reciprocals
+    // over several rows, because more workgroups keep more rows in flight.
+    hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1>), dim3(static_cast<unsigned>(a.M)), dim3(T), 0,
+                       stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx);
     return hipGetLastError();
 }
 
@@ -148,21 +270,21 @@ hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
-    const int64_t need = (a.K + 4 * QTHREADS - 1) / (4 * QTHREADS);  // float4 per thread
-    if (need <= 1) return launch_reg<1>(a, stream);
-    if (need <= 2) return launch_reg<2>(a, stream);
-    if (need <= 3) return launch_reg<3>(a, stream);
-    if (need <= 4) return launch_reg<4>(a, stream);
-    if (need <= 5) return launch_reg<5>(a, stream);
-    if (need <= 6) return launch_reg<6>(a, stream);
-    if (need <= 8) return launch_reg<8>(a, stream);
-    if (need <= 10) return launch_reg<10>(a, stream);
-    if (need <= 12) return launch_reg<12>(a, stream);
-    if (need <= 14) return launch_reg<14>(a, stream);
-    if (need <= 17) return launch_reg<17>(a, stream);
-    if (need <= 20) return launch_reg<20>(a, stream);
-    if (need <= 24) return launch_reg<24>(a, stream);
-    if (need <= 32) return launch_reg<32>(a, stream);
+    const int64_t n256 = (a.K + 1023) / 1024;   // float4 per thread with 256 threads
+    const int64_t n512 = (a.K + 2047) / 2048;   // ... with 512 threads
+    if (n256 <= 1) return launch_reg<1, 256>(a, stream);
+    if (n256 <= 2) return launch_reg<2, 256>(a, stream);
+    if (n256 <= 3) return launch_reg<3, 256>(a, stream);
+    if (n256 <= 4) return launch_reg<4, 256>(a, stream);
+    if (n256 <= 5) return launch_reg<5, 256>(a, stream);
+    if (n256 <= 6) return launch_reg<6, 256>(a, stream);
+    if (n512 <= 4) return launch_reg<4, 512>(a, stream);
+    if (n512 <= 5) return launch_reg<5, 512>(a, stream);
+    if (n512 <= 6) return launch_reg<6, 512>(a, stream);
+    if (n512 <= 8) return launch_reg<8, 512>(a, stream);
+    if (n512 <= 9) return launch_reg<9, 512>(a, stream);
+    if (n512 <= 12) return launch_reg<12, 512>(a, stream);
+    if (n512 <= 16) return launch_reg<16, 512>(a, stream);
     hipLaunchKernelGGL(quantize_rows_stream, dim3(static_cast<unsigned>(a.M)), dim3(QTHREADS), 0,
                        stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, a.xq, a.sx);
     return hipGetLastError();
