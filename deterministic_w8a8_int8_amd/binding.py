@@ -164,9 +164,9 @@ def w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) -> int:
 
 
 def splitk_workspace(M, N, K, splitk, device="cuda"):
-    """A zero-filled workspace of the size w8a8_gemm_splitk needs."""
+    """A workspace of the size w8a8_gemm_splitk needs (contents irrelevant)."""
     n = w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk)
-    return torch.zeros((max(n, 1),), dtype=torch.uint8, device=device)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
 
 
 def w8a8_gemm_splitk(xq, sx, w, sw, splitk, residual=None, y=None, workspace=None, stream=None):

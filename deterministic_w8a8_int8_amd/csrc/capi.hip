@@ -127,7 +127,7 @@ size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int spl
         M > kMaxDim || N > kMaxDim)
         return static_cast<size_t>(-1);
     if (splitk == 1 || M == 0 || N == 0) return 0;
-    return w8a8::gemm_workspace_bytes(w8a8::plan_gemm(M, N, K, splitk));
+    return w8a8::gemm_workspace_bytes(M, N, splitk);
 }
 
 int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,

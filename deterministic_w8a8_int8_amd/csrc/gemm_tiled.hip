@@ -33,15 +33,19 @@
 //     range of tiles, rastered in groups of `group_m` tile rows.  The tiles
 //     running together on one XCD then share A and B panels in that XCD's L2.
 //   - Split-K: blockIdx picks (tile, chunk).  Every chunk writes its int32
-//     partial tile to the workspace in register order: coalesced 256-byte
-//     wave stores.  It bumps the tile's arrival counter (an integer atomic
-//     on a counter, never on data).  The last arriver adds the other
-//     chunks' partials onto its own, resets the counter and runs the
-//     epilogue.  The int32 sum is exact, so the arrival order cannot change
-//     a bit.
+//     partial tile, row-major, to its own slice of the workspace through the
+//     same LDS-staged, coalesced path as the epilogue.  A second kernel on
+//     the same stream (splitk_reduce) adds the S slices of each output, in
+//     chunk order, and runs the epilogue.  No workgroup waits for another
+//     and no cache is flushed inside the GEMM: a device-scope fence per tile
+//     would write back and invalidate the XCD's L2 under the other
+//     workgroups' operand panels.  The int32 sum is exact, so neither the
+//     order nor S can change a bit.
 //   - The epilogue stages sx and sw of the tile in LDS.  It computes
 //     fl(fl(fl(float(acc))*sx)*sw) (+ r), rounding once per step, with no
 //     fused multiply-add (the whole file is built with -ffp-contract=off).
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -106,12 +110,14 @@ __device__ __forceinline__ void wait_fills() { asm volatile("s_waitcnt vmcnt(0)"
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// v_mfma_i32_32x32x32_i8 as inline asm: C += A * B on one 32x32 int32 tile
-// held in AGPRs.  The memory clobber pins it in program order relative to
-// the LDS reads and fills around it (the instruction schedule of the main
-// loop is written in the source).
+// v_mfma_i32_32x32x32_i8: C += A * B on one 32x32 int32 tile.  The builtin
+// lets the compiler place the accumulator (VGPR or AGPR) and insert the wait
+// states its result needs; the scheduling barrier after it keeps the
+// instruction order of the main loop as written in the source (MFMAs
+// interleaved with LDS reads and fills).
 __device__ __forceinline__ void mfma_32x32x32_i8(i32x16& c, const i32x4& a, const i32x4& b) {
-    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Generous wait states after the last MFMA before its results are read by
@@ -140,10 +146,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, const float* residual, float* y, int M, int N, int K,
     int tiles_m, int tiles_n, int group_m, int splitk, int kb_per_split,
-    int32_t* __restrict__ counters, int32_t* __restrict__ partials) {
+    int32_t* __restrict__ partials) {
     constexpr int WTM = C::WTM, WTN = C::WTN, BK = C::BK, NST = C::NST;
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS_BYTES];
-    __shared__ int last_flag;
 
     // ---- block -> (tile, split), XCD-contiguous and grouped along M
     const int nblocks = gridDim.x;
@@ -176,49 +181,48 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     const int lane = threadIdx.x & 63;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
 
-    // ---- per-lane global offsets for the LDS fills.  Instruction j of wave w
-    // fills LDS rows RPF*(w + NW*j) .. +RPF-1 (RPF = rows per fill, 1 KiB);
-    // lane l lands in row RPF*(w + NW*j) + l / CHUNKS at physical chunk
-    // l % CHUNKS, which holds logical chunk (l % CHUNKS) ^ swz(row).
+    // ---- LDS fills.  Instruction j of wave w fills LDS rows RPF*(w + NW*j) ..
+    // +RPF-1 (RPF = rows per fill, 1 KiB); lane l lands in row
+    // RPF*(w + NW*j) + l / CHUNKS at physical chunk l % CHUNKS, which holds
+    // logical chunk (l % CHUNKS) ^ swz(row).  With NW even, the swizzle of
+    // that row depends on the lane alone (RPF*NW is a multiple of 16), so a
+    // single per-lane byte offset serves every fill of A and of B.  The row
+    // group's base goes into the scalar address; only rows past the end of
+    // the matrix need a per-lane clamp, computed at the fill itself so that
+    // no per-fill offsets stay live across the main loop.
+    static_assert(C::NW % 2 == 0, "fill swizzle must not depend on the fill index");
     constexpr int RPF = C::ROWS_PER_FILL;
     const int lrow = lane / C::CHUNKS;
-    const int lphys = lane % C::CHUNKS;
-    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
-    int a_chunk[C::A_LOADS], b_chunk[C::B_LOADS];
-#pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j) {
-        const int r = RPF * (wave + C::NW * j) + lrow;
-        const int gr = min(row0 + r, M - 1);
-        a_chunk[j] = lphys ^ row_swz<C::CHUNKS>(r);
-        a_off[j] = static_cast<uint32_t>(gr - row0) * static_cast<uint32_t>(K) +
-                   static_cast<uint32_t>(a_chunk[j] * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < C::B_LOADS; ++j) {
-        const int r = RPF * (wave + C::NW * j) + lrow;
-        const int gc = min(col0 + r, N - 1);
-        b_chunk[j] = lphys ^ row_swz<C::CHUNKS>(r);
-        b_off[j] = static_cast<uint32_t>(gc - col0) * static_cast<uint32_t>(K) +
-                   static_cast<uint32_t>(b_chunk[j] * 16);
-    }
-    const int8_t* a_base = A + static_cast<int64_t>(row0) * K + kb0 * 64;
-    const int8_t* b_base = B + static_cast<int64_t>(col0) * K + kb0 * 64;
+    const int lchunk = (lane % C::CHUNKS) ^ row_swz<C::CHUNKS>(RPF * wave + lrow);
+    const uint32_t koff = static_cast<uint32_t>(lchunk * 16);
+    // A half stage (BK = 128, odd number of k-blocks) must not read past the
+    // chunk or the matrix: lanes of the upper half re-read the lower half,
+    // whose bytes are valid and are never multiplied.
+    const uint32_t koff_half = lchunk >= 4 ? koff - 64u : koff;
+    const int8_t* a_k = A + kb0 * 64;
+    const int8_t* b_k = B + kb0 * 64;
 
-    auto issue = [&](int st, int buf) {
-        // A half stage (BK = 128, odd number of k-blocks) must not read past
-        // the chunk or the matrix: lanes of the upper half re-read the lower
-        // half, whose bytes are valid and are never multiplied.
+    // One fill instruction of stage st into buffer buf: index d over the A
+    // fills, then the B fills.
+    auto issue_one = [&](int st, int buf, int d) {
         const bool half = half_last && (st == nst - 1);
-        const int8_t* ga = a_base + st * BK;
-        const int8_t* gb = b_base + st * BK;
-        lds_i8* la = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK;
-        lds_i8* lb = la + C::A_BYTES;
+        const bool is_a = d < C::A_LOADS;
+        const int j = is_a ? d : d - C::A_LOADS;
+        const int first = is_a ? row0 : col0;
+        const int rows = is_a ? M : N;
+        int grow = min(first + RPF * (wave + C::NW * j), rows - 1);   // uniform
+        asm volatile("" : "+s"(grow));  // recomputed per fill, never hoisted
+        const int lim = rows - 1 - grow;
+        const uint32_t voff = static_cast<uint32_t>(min(lrow, lim)) * static_cast<uint32_t>(K) +
+                              (half ? koff_half : koff);
+        const int8_t* g = (is_a ? a_k : b_k) + static_cast<int64_t>(grow) * K + st * BK;
+        lds_i8* dst = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK +
+                      (is_a ? 0 : C::A_BYTES) + RPF * C::NW * j * BK;
+        lds_fill16(g, voff, dst);
+    };
+    auto issue = [&](int st, int buf) {
 #pragma unroll
-        for (int j = 0; j < C::A_LOADS; ++j)
-            lds_fill16(ga, a_off[j] - ((half && a_chunk[j] >= 4) ? 64u : 0u), la + RPF * C::NW * j * BK);
-#pragma unroll
-        for (int j = 0; j < C::B_LOADS; ++j)
-            lds_fill16(gb, b_off[j] - ((half && b_chunk[j] >= 4) ? 64u : 0u), lb + RPF * C::NW * j * BK);
+        for (int d = 0; d < C::LPS; ++d) issue_one(st, buf, d);
     };
 
     // ---- per-lane LDS read offsets for the MFMA operands.  Fragment i of this
@@ -252,21 +256,6 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             f.b[q - WTM] =
                 *reinterpret_cast<const i32x4*>(lb + b_row_off + (q - WTM) * 32 * BK + chunk_off[s]);
     };
-    // One fill instruction of stage st into buffer buf: index d over the A
-    // fills, then the B fills.
-    auto issue_one = [&](int st, int buf, int d) {
-        const bool half = half_last && (st == nst - 1);
-        lds_i8* la = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK;
-        if (d < C::A_LOADS) {
-            lds_fill16(a_base + st * BK, a_off[d] - ((half && a_chunk[d] >= 4) ? 64u : 0u),
-                       la + RPF * C::NW * d * BK);
-        } else {
-            const int e = d - C::A_LOADS;
-            lds_fill16(b_base + st * BK, b_off[e] - ((half && b_chunk[e] >= 4) ? 64u : 0u),
-                       la + C::A_BYTES + RPF * C::NW * e * BK);
-        }
-    };
-
     // ---- main loop: NST - 1 stages in flight.  At iteration st the wave waits
     // until its copies of stage st have landed (later stages may still be
     // pending); the barrier publishes stage st to every wave and frees the
@@ -410,50 +399,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     }
     mfma_drain();
 
-    // ---- integer split-K: the last chunk of a tile to finish adds the others
-    if (splitk > 1) {
-        const int ntiles = tiles_m * tiles_n;
-        const size_t tile_elems = static_cast<size_t>(C::BM) * C::BN;
-        int32_t* mine = partials + (static_cast<size_t>(split) * ntiles + tile) * tile_elems +
-                        static_cast<size_t>(wave) * C::ACC_PER_WAVE;
-#pragma unroll
-        for (int i = 0; i < WTM; ++i)
-#pragma unroll
-            for (int j = 0; j < WTN; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mine[((i * WTN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
-        wait_fills();
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) last_flag = (atomicAdd(&counters[tile], 1) == splitk - 1);
-        __syncthreads();
-        if (!last_flag) return;
-        __threadfence();
-        if (threadIdx.x == 0) counters[tile] = 0;
-        // Integer addition is exact and associative, so adding the other
-        // chunks onto this block's own partial (in increasing c) gives the
-        // same int32 as P_0 + P_1 + ... + P_{S-1}.  One 32x32 accumulator at
-        // a time keeps the register footprint small.
-        const int32_t* p0 = partials + static_cast<size_t>(tile) * tile_elems +
-                            static_cast<size_t>(wave) * C::ACC_PER_WAVE;
-        const size_t cstride = static_cast<size_t>(ntiles) * tile_elems;
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-#pragma unroll
-            for (int j = 0; j < WTN; ++j) {
-                i32x16 v = acc[i][j];
-                const int32_t* pj = p0 + ((i * WTN + j) * 16) * 64 + lane;
-                for (int c = 0; c < splitk; ++c) {
-                    if (c == split) continue;
-                    const int32_t* pc = pj + c * cstride;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) v[e] += pc[e * 64];
-                }
-                acc[i][j] = v;
-                sched_fence();
-            }
-        }
-    }
+    // ---- integer split-K: this chunk's raw int32 partial goes, row-major,
+    // to slice `split` of the workspace instead of the epilogue
+    int32_t* part = partials ? partials + static_cast<size_t>(split) * static_cast<size_t>(M) *
+                                              static_cast<size_t>(N)
+                             : nullptr;
 
     if constexpr (C::DIRECT_EPI) {
         // ---- epilogue straight from the accumulators: for a fixed element e,
@@ -477,7 +427,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     const int row = row0 + wm * 32 * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                     if (full || (row < M && col < N)) {
                         const size_t o = static_cast<size_t>(row) * N + col;
-                        y[o] = residual ? scale_acc_residual(acc[i][j][e], sxv[e], swn, residual[o])
+                        if (part) part[o] = acc[i][j][e];
+                        else y[o] = residual ? scale_acc_residual(acc[i][j][e], sxv[e], swn, residual[o])
                                         : scale_acc(acc[i][j][e], sxv[e], swn);
                     }
                 }
@@ -501,8 +452,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
     for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
 
-    const bool vec_ok = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
-                        (reinterpret_cast<uintptr_t>(residual) & 15) == 0;
+    // (a partial slice starts 16-byte aligned whenever N % 4 == 0: the
+    // workspace is 256-byte aligned)
+    const bool vec_ok = (N & 3) == 0 &&
+                        (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                                  (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
     constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
     constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
     const int c4 = threadIdx.x % C4;
@@ -532,6 +486,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             const float sxm = s_sx[lr];
             const size_t o = static_cast<size_t>(row) * N + col;
             if (vec_ok && col + 3 < N) {
+                if (part) {
+                    *reinterpret_cast<int4*>(part + o) = a4;
+                    continue;
+                }
                 float4 v;
                 if (residual) {
                     const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
@@ -551,15 +509,87 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    if (col + q < N) {
-                        y[o + q] = residual ? scale_acc_residual(av[q], sxm, swv[q], residual[o + q])
-                                            : scale_acc(av[q], sxm, swv[q]);
-                    }
+                    if (col + q >= N) continue;
+                    if (part) part[o + q] = av[q];
+                    else y[o + q] = residual ? scale_acc_residual(av[q], sxm, swv[q], residual[o + q])
+                                             : scale_acc(av[q], sxm, swv[q]);
                 }
             }
         }
         __syncthreads();
     }
+}
+
+// ---- split-K reduction and epilogue: y = epi(P_0 + P_1 + ... + P_{S-1}).
+// An HBM-bound stream (4S bytes of partials (+4 of residual) read and 4
+// written per output).  VEC: one thread per 4 consecutive outputs of a row,
+// for N % 4 == 0 and 16-byte aligned float buffers; else one per output.
+// The residual may be y itself: each output is read and written by the
+// same thread.
+constexpr int REDUCE_THREADS = 256;
+
+template <bool VEC>
+__global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce(
+    const int32_t* __restrict__ P, int S, const float* __restrict__ sx,
+    const float* __restrict__ sw, const float* residual, float* y, int64_t M, int64_t N) {
+    const int64_t MN = M * N;
+    const int64_t units = VEC ? MN / 4 : MN;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * REDUCE_THREADS;
+    for (int64_t u = static_cast<int64_t>(blockIdx.x) * REDUCE_THREADS + threadIdx.x; u < units;
+         u += stride) {
+        if constexpr (VEC) {
+            const int64_t o = 4 * u;
+            const int64_t m = o / N;
+            const int64_t n = o - m * N;
+            i32x4 a = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(P + o));
+#pragma unroll 4
+            for (int c = 1; c < S; ++c)
+                a += __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(P + c * MN + o));
+            const float sxm = sx[m];
+            const float4 sw4 = *reinterpret_cast<const float4*>(sw + n);
+            float4 v;
+            if (residual) {
+                const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
+                v.x = scale_acc_residual(a[0], sxm, sw4.x, r4.x);
+                v.y = scale_acc_residual(a[1], sxm, sw4.y, r4.y);
+                v.z = scale_acc_residual(a[2], sxm, sw4.z, r4.z);
+                v.w = scale_acc_residual(a[3], sxm, sw4.w, r4.w);
+            } else {
+                v.x = scale_acc(a[0], sxm, sw4.x);
+                v.y = scale_acc(a[1], sxm, sw4.y);
+                v.z = scale_acc(a[2], sxm, sw4.z);
+                v.w = scale_acc(a[3], sxm, sw4.w);
+            }
+            *reinterpret_cast<float4*>(y + o) = v;
+        } else {
+            const int64_t m = u / N;
+            const int64_t n = u - m * N;
+            int32_t a = P[u];
+            for (int c = 1; c < S; ++c) a += P[c * MN + u];
+            y[u] = residual ? scale_acc_residual(a, sx[m], sw[n], residual[u])
+                            : scale_acc(a, sx[m], sw[n]);
+        }
+    }
+}
+
+hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipStream_t stream) {
+    const int64_t MN = a.M * a.N;
+    const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.sw) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.residual) & 15) == 0;
+    const int64_t units = vec ? MN / 4 : MN;
+    // about 4 units per thread with at most 32 workgroups per CU resident
+    const int64_t blocks = std::max<int64_t>(
+        1, std::min<int64_t>((units + 4 * REDUCE_THREADS - 1) / (4 * REDUCE_THREADS), 256 * 32));
+    if (vec)
+        hipLaunchKernelGGL((splitk_reduce<true>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(REDUCE_THREADS), 0, stream, partials, S, a.sx, a.sw, a.residual,
+                           a.y, a.M, a.N);
+    else
+        hipLaunchKernelGGL((splitk_reduce<false>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(REDUCE_THREADS), 0, stream, partials, S, a.sx, a.sw, a.residual,
+                           a.y, a.M, a.N);
+    return hipGetLastError();
 }
 
 // The configurations, indexed by TileKind.
@@ -575,20 +605,15 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hip
     const int64_t ntiles = p.tiles_m * p.tiles_n;
     const int KB = static_cast<int>(a.K >> 6);
     const int kb_per_split = (KB + p.splitk - 1) / p.splitk;
-    int32_t* counters = nullptr;
-    int32_t* partials = nullptr;
-    if (p.splitk > 1) {
-        counters = static_cast<int32_t*>(workspace);
-        const size_t cbytes = ((static_cast<size_t>(ntiles) * 4 + 255) / 256) * 256;
-        partials = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cbytes);
-    }
+    int32_t* partials = p.splitk > 1 ? static_cast<int32_t*>(workspace) : nullptr;
     const unsigned nblocks = static_cast<unsigned>(ntiles * p.splitk);
     hipLaunchKernelGGL((gemm_tiled<C>), dim3(nblocks), dim3(C::THREADS), 0, stream, a.xq, a.sx, a.w,
                        a.sw, a.residual, a.y, static_cast<int>(a.M), static_cast<int>(a.N),
                        static_cast<int>(a.K), static_cast<int>(p.tiles_m),
-                       static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, counters,
-                       partials);
-    return hipGetLastError();
+                       static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, partials);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splitk <= 1) return e;
+    return launch_reduce(a, p.splitk, partials, stream);
 }
 
 struct KindInfo {
@@ -646,11 +671,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
     return p;
 }
 
-size_t gemm_workspace_bytes(const GemmPlan& p) {
-    if (p.splitk <= 1) return 0;
-    const size_t ntiles = static_cast<size_t>(p.tiles_m * p.tiles_n);
-    const size_t cbytes = ((ntiles * 4 + 255) / 256) * 256;
-    return cbytes + static_cast<size_t>(p.splitk) * ntiles * p.bm * p.bn * 4;
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk) {
+    if (splitk <= 1) return 0;
+    // S row-major int32 slices of the output, rounded up to 256 bytes
+    const size_t bytes = static_cast<size_t>(splitk) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
+    return (bytes + 255) / 256 * 256;
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,

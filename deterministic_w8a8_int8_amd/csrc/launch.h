@@ -53,7 +53,7 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk);
 void set_tile_override(int kind);
-size_t gemm_workspace_bytes(const GemmPlan& p);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,
                              hipStream_t stream);
 

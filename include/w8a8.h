@@ -166,19 +166,18 @@ size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int spl
  *     P_c[m,n] = sum over chunk c of xq[m,k]*w[n,k]      (int32)
  *     acc      = P_0 + P_1 + ... + P_{splitk-1}           (int32)
  * followed by the same epilogue as w8a8_gemm.  No floating-point atomic is
- * used anywhere.  Partials go through the workspace as int32, and the last
- * chunk of a tile to finish adds the others onto its own.  Integer addition
- * is exact and associative, so neither that order nor splitk can change a
- * bit: the output is bit-identical to w8a8_gemm.
+ * used anywhere.  Each chunk writes P_c as int32 to its own slice of the
+ * workspace; a second kernel on the same stream adds the slices in chunk
+ * order and runs the epilogue.  Integer addition is exact and associative,
+ * so neither that order nor splitk can change a bit: the output is
+ * bit-identical to w8a8_gemm.
  *
  * splitk     1 <= splitk <= W8A8_MAX_SPLITK.
  * workspace  device, 256-byte aligned, at least
- *            w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) bytes.
- *            Its first bytes hold per-tile arrival counters.  They must be
- *            zero before the first call (allocate with hipMemset or
- *            torch.zeros).  Every call leaves them zero again.  So one
- *            workspace serves any later call of the same or smaller size,
- *            as long as calls that share it do not overlap in time.
+ *            w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) bytes
+ *            (splitk * M * N int32 partials).  Its contents on entry do not
+ *            matter and are overwritten; calls that share one workspace
+ *            must not overlap in time.  Ignored when splitk == 1.
  * Other arguments as for w8a8_gemm.
  */
 int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,

@@ -132,8 +132,9 @@ def test_splitk_matches_oracle(M, N, K, splitk):
     xq, sx, w, sw, r = _gemm_case(M, N, K, seed=3 * M + N, residual=True)
     want = oracle.gemm(xq, sx, w, sw, r)
     ws = B.splitk_workspace(M, N, K, splitk)
+    ws.fill_(0xA5)  # whatever the workspace holds on entry is overwritten
     xq_d, sx_d, w_d, sw_d, r_d = dev(xq), dev(sx), dev(w), dev(sw), dev(r)
-    for rep in range(2):  # the workspace counters must come back to zero
+    for rep in range(2):  # and it serves the next call as it is left
         got = host(B.w8a8_gemm_splitk(xq_d, sx_d, w_d, sw_d, splitk, residual=r_d, workspace=ws))
         assert_bits_equal(got, want, f"split {splitk} rep {rep}")
 
@@ -152,6 +153,9 @@ def test_residual_in_place():
     rd = dev(r)
     B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=rd, y=rd)
     assert_bits_equal(host(rd), want, "in place")
+    rd = dev(r)
+    B.w8a8_gemm_splitk(dev(xq), dev(sx), dev(w), dev(sw), 2, residual=rd, y=rd)
+    assert_bits_equal(host(rd), want, "in place, split 2")
 
 
 def test_rows_identical_across_kernels_and_batches():
