@@ -27,7 +27,11 @@
 //     for either 32 or 64 LDS banks.
 //   - Integer accumulation is exact, so any lane -> k assignment gives the
 //     same sum, provided A and B use the same one.  Only the placement of the
-//     32 x 32 result tile matters.
+//     32 x 32 result tile matters.  The weight fragment is the MFMA's first
+//     operand, so each tile holds the transposed block: lane l, element e is
+//     output row (l % 32) and column 8*(e/4) + 4*(l/32) + e%4.  Four
+//     consecutive elements are four adjacent columns of one row, written
+//     with one 16-byte store.
 //   - Block ids are renumbered for the 8 XCDs: the hardware deals workgroups
 //     round-robin over XCDs, and the renumbering gives each XCD a contiguous
 //     range of tiles, rastered in groups of `group_m` tile rows.  The tiles
@@ -81,7 +85,7 @@ struct Cfg {
     static constexpr int SUBSTEPS = BK / 32;          // MFMA K-steps per stage
     static constexpr int ACC_PER_WAVE = WTM * WTN * 16 * 64;  // int32 per wave
     static constexpr int STAGED_ROWS = 32 * WGM;      // epilogue rows per pass
-    static constexpr int LDR = BN + 8;                // staged row pitch (int32)
+    static constexpr int LDR = BN + 4;                // staged row pitch (int32), 4 mod 64 banks
     static constexpr int EPI_BYTES = STAGED_ROWS * LDR * 4 + (BM + BN) * 4;
     static constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
     static_assert(A_LOADS * ROWS_PER_FILL * NW == BM && B_LOADS * ROWS_PER_FILL * NW == BN,
@@ -110,13 +114,14 @@ __device__ __forceinline__ void wait_fills() { asm volatile("s_waitcnt vmcnt(0)"
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// v_mfma_i32_32x32x32_i8: C += A * B on one 32x32 int32 tile.  The builtin
-// lets the compiler place the accumulator (VGPR or AGPR) and insert the wait
-// states its result needs; the scheduling barrier after it keeps the
-// instruction order of the main loop as written in the source (MFMAs
-// interleaved with LDS reads and fills).
-__device__ __forceinline__ void mfma_32x32x32_i8(i32x16& c, const i32x4& a, const i32x4& b) {
-    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+// One v_mfma_i32_32x32x32_i8 on a 32x32 int32 tile: c += w_frag * x_frag^T,
+// i.e. the weight rows index the tile's first dimension (see the layout note
+// at the top).  The builtin lets the compiler place the accumulator and
+// insert the wait states its result needs; the scheduling barrier after it
+// keeps the instruction order of the main loop as written in the source
+// (MFMAs interleaved with LDS reads and fills).
+__device__ __forceinline__ void mfma_32x32x32_i8(i32x16& c, const i32x4& x_frag, const i32x4& w_frag) {
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(w_frag, x_frag, c, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -185,11 +190,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     // +RPF-1 (RPF = rows per fill, 1 KiB); lane l lands in row
     // RPF*(w + NW*j) + l / CHUNKS at physical chunk l % CHUNKS, which holds
     // logical chunk (l % CHUNKS) ^ swz(row).  With NW even, the swizzle of
-    // that row depends on the lane alone (RPF*NW is a multiple of 16), so a
-    // single per-lane byte offset serves every fill of A and of B.  The row
-    // group's base goes into the scalar address; only rows past the end of
-    // the matrix need a per-lane clamp, computed at the fill itself so that
-    // no per-fill offsets stay live across the main loop.
+    // that row depends on the lane alone (RPF*NW is a multiple of 16).
+    // Per-lane byte offsets (rows past the end of the matrix clamped to its
+    // last row) are computed once; a stage then costs two scalar adds per
+    // operand, and one fill instruction about four instructions, so that a
+    // fill fits in the issue slots of one MFMA.
     static_assert(C::NW % 2 == 0, "fill swizzle must not depend on the fill index");
     constexpr int RPF = C::ROWS_PER_FILL;
     const int lrow = lane / C::CHUNKS;
@@ -198,31 +203,48 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     // A half stage (BK = 128, odd number of k-blocks) must not read past the
     // chunk or the matrix: lanes of the upper half re-read the lower half,
     // whose bytes are valid and are never multiplied.
-    const uint32_t koff_half = lchunk >= 4 ? koff - 64u : koff;
-    const int8_t* a_k = A + kb0 * 64;
-    const int8_t* b_k = B + kb0 * 64;
+    const uint32_t half_adj = lchunk >= 4 ? 64u : 0u;
+    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+#pragma unroll
+    for (int j = 0; j < C::A_LOADS; ++j) {
+        const int gr = min(row0 + RPF * (wave + C::NW * j) + lrow, M - 1);
+        a_off[j] = static_cast<uint32_t>(gr - row0) * static_cast<uint32_t>(K) + koff;
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_LOADS; ++j) {
+        const int gc = min(col0 + RPF * (wave + C::NW * j) + lrow, N - 1);
+        b_off[j] = static_cast<uint32_t>(gc - col0) * static_cast<uint32_t>(K) + koff;
+    }
+    const int8_t* a_tile = A + static_cast<int64_t>(row0) * K + kb0 * 64;
+    const int8_t* b_tile = B + static_cast<int64_t>(col0) * K + kb0 * 64;
+    lds_i8* const l_wave = (lds_i8*)smem + RPF * wave * BK;
 
-    // One fill instruction of stage st into buffer buf: index d over the A
-    // fills, then the B fills.
-    auto issue_one = [&](int st, int buf, int d) {
+    // Where stage st goes: scalar sources, this wave's LDS slice of buffer
+    // buf, and the half-stage lane adjustment.
+    struct FillStage {
+        const int8_t* ga;
+        const int8_t* gb;
+        lds_i8* l;
+        uint32_t adj;
+    };
+    auto fill_stage = [&](int st, int buf) -> FillStage {
         const bool half = half_last && (st == nst - 1);
-        const bool is_a = d < C::A_LOADS;
-        const int j = is_a ? d : d - C::A_LOADS;
-        const int first = is_a ? row0 : col0;
-        const int rows = is_a ? M : N;
-        int grow = min(first + RPF * (wave + C::NW * j), rows - 1);   // uniform
-        asm volatile("" : "+s"(grow));  // recomputed per fill, never hoisted
-        const int lim = rows - 1 - grow;
-        const uint32_t voff = static_cast<uint32_t>(min(lrow, lim)) * static_cast<uint32_t>(K) +
-                              (half ? koff_half : koff);
-        const int8_t* g = (is_a ? a_k : b_k) + static_cast<int64_t>(grow) * K + st * BK;
-        lds_i8* dst = (lds_i8*)smem + buf * C::STAGE + RPF * wave * BK +
-                      (is_a ? 0 : C::A_BYTES) + RPF * C::NW * j * BK;
-        lds_fill16(g, voff, dst);
+        return FillStage{a_tile + st * BK, b_tile + st * BK, l_wave + buf * C::STAGE,
+                         half ? half_adj : 0u};
+    };
+    // Fill instruction d of a stage: the A fills, then the B fills.
+    auto issue_one = [&](const FillStage& f, int d) {
+        if (d < C::A_LOADS) {
+            lds_fill16(f.ga, a_off[d] - f.adj, f.l + RPF * C::NW * d * BK);
+        } else {
+            const int e = d - C::A_LOADS;
+            lds_fill16(f.gb, b_off[e] - f.adj, f.l + C::A_BYTES + RPF * C::NW * e * BK);
+        }
     };
     auto issue = [&](int st, int buf) {
+        const FillStage f = fill_stage(st, buf);
 #pragma unroll
-        for (int d = 0; d < C::LPS; ++d) issue_one(st, buf, d);
+        for (int d = 0; d < C::LPS; ++d) issue_one(f, d);
     };
 
     // ---- per-lane LDS read offsets for the MFMA operands.  Fragment i of this
@@ -306,6 +328,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             const int8_t* lb = la + C::A_BYTES;
             const int8_t* la_n = smem + ((st + 1) % NST) * C::STAGE;
             const int8_t* lb_n = la_n + C::A_BYTES;
+            const FillStage fs = fill_stage(st + NST - 1, (st + NST - 1) % NST);
             int q = 0, d = 0;
             // sub-step 0: MFMAs on f0; read sub-step 1 into f1; copy stage st+NST-1
 #pragma unroll
@@ -315,7 +338,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     mfma_32x32x32_i8(acc[i][j], f0.a[i], f0.b[j]);
                     if (q < WTM + WTN) load_frag(f1, la, lb, 1, q++);
                     if (d < C::LPS) {
-                        if (fill) issue_one(st + NST - 1, (st + NST - 1) % NST, d);
+                        if (fill) issue_one(fs, d);
                         ++d;
                     }
                 }
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             for (; q < WTM + WTN; ++q) load_frag(f1, la, lb, 1, q);
 #pragma unroll
             for (; d < C::LPS; ++d)
-                if (fill) issue_one(st + NST - 1, (st + NST - 1) % NST, d);
+                if (fill) issue_one(fs, d);
             // sub-step 1: MFMAs on f1; read the next stage's sub-step 0 into f0
             q = 0;
 #pragma unroll
@@ -361,8 +384,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 wait_vm<0>();
             }
             __syncthreads();
-            const bool fill = st + NST - 1 < nst;
-            const int fill_st = st + NST - 1, fill_buf = (st + NST - 1) % NST;
+            // The copy of stage st + NST - 1 is issued unconditionally, with
+            // the stage clamped to the last one: past the end it re-reads
+            // bytes in bounds into a buffer nobody reads again, which keeps
+            // a branch out of every fill.  All copies land before the
+            // epilogue reuses the LDS (wait_fills after the loop).
+            const FillStage fs = fill_stage(min(st + NST - 1, nst - 1), (st + NST - 1) % NST);
             const int8_t* la = smem + (st % NST) * C::STAGE;
             const int8_t* lb = la + C::A_BYTES;
             const int nsub = (half_last && st == nst - 1) ? 2 : C::SUBSTEPS;
@@ -382,22 +409,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     for (int j = 0; j < WTN; ++j) {
                         mfma_32x32x32_i8(acc[i][j], cur.a[i], cur.b[j]);
                         if (s + 1 < C::SUBSTEPS && q < WTM + WTN) load_frag(nxt, la, lb, s + 1, q++);
-                        if (d < C::LPS) {
-                            if (fill) issue_one(fill_st, fill_buf, d);
-                            ++d;
-                        }
+                        if (d < C::LPS) issue_one(fs, d++);
                     }
                 }
                 if (s + 1 < C::SUBSTEPS) {
                     while (q < WTM + WTN) load_frag(nxt, la, lb, s + 1, q++);
                 }
             }
-            if (fill) {
-                while (d < C::LPS) issue_one(fill_st, fill_buf, d++);
-            }
+            while (d < C::LPS) issue_one(fs, d++);
         }
     }
     mfma_drain();
+    wait_fills();
 
     // ---- integer split-K: this chunk's raw int32 partial goes, row-major,
     // to slice `split` of the workspace instead of the epilogue
@@ -406,30 +429,59 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                              : nullptr;
 
     if constexpr (C::DIRECT_EPI) {
-        // ---- epilogue straight from the accumulators: for a fixed element e,
-        // lanes 0-31 write 32 consecutive floats (128 bytes) of one row and
-        // lanes 32-63 the same of the row 4 below.  No LDS and no barrier.
-        const bool full = (row0 + C::BM <= M) && (col0 + C::BN <= N);
+        // ---- epilogue straight from the accumulators: every lane writes four
+        // adjacent outputs of its row per 16-byte store.  No LDS, no barrier.
+        const bool vec_ok = (N & 3) == 0 &&
+                            (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                                      (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
+        float swv[WTN][16];
 #pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-            float sxv[16];
+        for (int j = 0; j < WTN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = row0 + wm * 32 * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                sxv[e] = sx[min(row, M - 1)];
+                const int col = col0 + wn * 32 * WTN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                swv[j][e] = sw[min(col, N - 1)];
             }
 #pragma unroll
-            for (int j = 0; j < WTN; ++j) {
-                const int col = col0 + wn * 32 * WTN + j * 32 + (lane & 31);
-                const float swn = sw[min(col, N - 1)];
+        for (int i = 0; i < WTM; ++i) {
+            const int row = row0 + wm * 32 * WTM + i * 32 + (lane & 31);
+            if (row >= M) continue;
+            const float sxm = sx[row];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = row0 + wm * 32 * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (full || (row < M && col < N)) {
-                        const size_t o = static_cast<size_t>(row) * N + col;
-                        if (part) part[o] = acc[i][j][e];
-                        else y[o] = residual ? scale_acc_residual(acc[i][j][e], sxv[e], swn, residual[o])
-                                        : scale_acc(acc[i][j][e], sxv[e], swn);
+            for (int j = 0; j < WTN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = col0 + wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                    const size_t o = static_cast<size_t>(row) * N + col;
+                    const i32x4 a = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                     acc[i][j][4 * g + 3]};
+                    if (vec_ok && col + 3 < N) {
+                        if (part) {
+                            *reinterpret_cast<i32x4*>(part + o) = a;
+                            continue;
+                        }
+                        float4 v;
+                        if (residual) {
+                            const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
+                            v.x = scale_acc_residual(a[0], sxm, swv[j][4 * g], r4.x);
+                            v.y = scale_acc_residual(a[1], sxm, swv[j][4 * g + 1], r4.y);
+                            v.z = scale_acc_residual(a[2], sxm, swv[j][4 * g + 2], r4.z);
+                            v.w = scale_acc_residual(a[3], sxm, swv[j][4 * g + 3], r4.w);
+                        } else {
+                            v.x = scale_acc(a[0], sxm, swv[j][4 * g]);
+                            v.y = scale_acc(a[1], sxm, swv[j][4 * g + 1]);
+                            v.z = scale_acc(a[2], sxm, swv[j][4 * g + 2]);
+                            v.w = scale_acc(a[3], sxm, swv[j][4 * g + 3]);
+                        }
+                        *reinterpret_cast<float4*>(y + o) = v;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (col + q >= N) continue;
+                            if (part) part[o + q] = a[q];
+                            else y[o + q] = residual ? scale_acc_residual(a[q], sxm, swv[j][4 * g + q], residual[o + q])
+                                                     : scale_acc(a[q], sxm, swv[j][4 * g + q]);
+                        }
                     }
                 }
                 sched_fence();
@@ -439,11 +491,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     }
 
     // ---- epilogue, in WTM passes of STAGED_ROWS rows.  Every wave parks one
-    // 32-row slice of its accumulators in LDS (row-major int32, rows padded
-    // by 8 words so the two half-waves of a ds_write land in different
-    // banks).  Then all threads sweep the slice in float4 chunks along rows,
-    // one 16-byte residual load and one 16-byte output store per chunk,
-    // fully coalesced.
+    // 32-row slice of its accumulators in LDS (row-major int32, four adjacent
+    // columns per 16-byte write; rows padded by 4 words so that the 16 lanes
+    // of one write phase, 16 different rows, hit 16 different bank groups).
+    // Then all threads sweep the slice in float4 chunks along rows, one
+    // 16-byte residual load and one 16-byte output store per chunk, fully
+    // coalesced.
     constexpr int LDR = C::LDR;
     int32_t* stage = reinterpret_cast<int32_t*>(smem);
     float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
@@ -459,24 +512,75 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                                   (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
     constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
     constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
+    constexpr int RPT = C::STAGED_ROWS / ROWS_PER_SWEEP;   // staged rows per thread
+    static_assert(C::STAGED_ROWS % ROWS_PER_SWEEP == 0, "epilogue sweep");
     const int c4 = threadIdx.x % C4;
     const int rsub = threadIdx.x / C4;
     const int col = col0 + 4 * c4;
+    // Interior tile with aligned rows: a straight-line sweep, every LDS read
+    // issued before the first store.  Otherwise the checked loop below.
+    const bool fast = vec_ok && row0 + C::BM <= M && col0 + C::BN <= N;
 #pragma unroll
     for (int pass = 0; pass < WTM; ++pass) {
         // accumulator slice i = pass of every wave -> staged rows wm*32 + r
+        const int lr = wm * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < WTN; ++j) {
-            const int lc = wn * 32 * WTN + j * 32 + (lane & 31);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int lr = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                stage[lr * LDR + lc] = acc[pass][j][e];
+            for (int g = 0; g < 4; ++g) {
+                const int lc = wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) =
+                    i32x4{acc[pass][j][4 * g], acc[pass][j][4 * g + 1], acc[pass][j][4 * g + 2],
+                          acc[pass][j][4 * g + 3]};
             }
             sched_fence();
         }
         __syncthreads();
         const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
+        if (fast) {
+            // staged row r = rsub + k * ROWS_PER_SWEEP is tile row
+            // (r / 32) * 32 * WTM + pass * 32 + r % 32
+            i32x4 av[RPT];
+            float sxv[RPT];
+            size_t ov[RPT];
+#pragma unroll
+            for (int k = 0; k < RPT; ++k) {
+                const int r = rsub + k * ROWS_PER_SWEEP;
+                const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
+                av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
+                sxv[k] = s_sx[lr];
+                ov[k] = static_cast<size_t>(row0 + lr) * N + col;
+            }
+            if (part) {
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) *reinterpret_cast<i32x4*>(part + ov[k]) = av[k];
+            } else if (residual) {
+                float4 rv[RPT];
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) rv[k] = *reinterpret_cast<const float4*>(residual + ov[k]);
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) {
+                    float4 v;
+                    v.x = scale_acc_residual(av[k][0], sxv[k], sw4.x, rv[k].x);
+                    v.y = scale_acc_residual(av[k][1], sxv[k], sw4.y, rv[k].y);
+                    v.z = scale_acc_residual(av[k][2], sxv[k], sw4.z, rv[k].z);
+                    v.w = scale_acc_residual(av[k][3], sxv[k], sw4.w, rv[k].w);
+                    *reinterpret_cast<float4*>(y + ov[k]) = v;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < RPT; ++k) {
+                    float4 v;
+                    v.x = scale_acc(av[k][0], sxv[k], sw4.x);
+                    v.y = scale_acc(av[k][1], sxv[k], sw4.y);
+                    v.z = scale_acc(av[k][2], sxv[k], sw4.z);
+                    v.w = scale_acc(av[k][3], sxv[k], sw4.w);
+                    *reinterpret_cast<float4*>(y + ov[k]) = v;
+                }
+            }
+            __syncthreads();
+            continue;
+        }
         for (int r = rsub; r < C::STAGED_ROWS; r += ROWS_PER_SWEEP) {
             // staged row r is tile row (r / 32) * 32 * WTM + pass * 32 + r % 32
             const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
