@@ -102,6 +102,14 @@ class Timer:
         ps = self.pairs.get(name, [])
         return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ps])) if ps else None
 
+    def pct_us(self, name):
+        """Median, 10th and 90th percentile of the launch durations (us)."""
+        ts = np.array([1e3 * a.elapsed_time(b) for a, b in self.pairs.get(name, [])])
+        if ts.size == 0:
+            return None
+        p10, p50, p90 = np.percentile(ts, [10, 50, 90])
+        return {"median": round(float(p50), 2), "p10": round(float(p10), 2), "p90": round(float(p90), 2)}
+
     def clear(self):
         self.pairs = {}
 
@@ -131,6 +139,48 @@ def cpu_baseline(gu, dn, head, cand, seconds):
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"first {R} of {gu['M']} tokens through both layers plus the read-out "
                       f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
+
+
+def mid_m_shapes(torch, B, stream_read_gbs):
+    """The short-request (M = 256) and forest-batch (M = 328) projections:
+    near the ridge of the int8 roofline, so each reports its time against
+    max(ops / MFMA peak, bytes / HBM peak).  Uniform random int8 operands."""
+    shapes = [("short_request_gate_up", 256, 34816, 5120, False, 1),
+              ("short_request_down", 256, 5120, 17408, True, 1),
+              ("short_request_down_splitk8", 256, 5120, 17408, True, 8),
+              ("forest_qkv_like", 328, 15360, 5120, False, 1),
+              ("forest_gate_up", 328, 34816, 5120, False, 1)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    out = {}
+    for name, M, N, K, res, S in shapes:
+        xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        sx = torch.rand(M, device="cuda", generator=g) * 0.01 + 1e-3
+        sw = torch.rand(N, device="cuda", generator=g) * 0.01 + 1e-3
+        r = torch.randn(M, N, device="cuda", generator=g) if res else None
+        y = torch.empty(M, N, device="cuda")
+        ws = B.splitk_workspace(M, N, K, S) if S > 1 else None
+        fn = (lambda: B.w8a8_gemm(xq, sx, w, sw, residual=r, y=y)) if S == 1 else \
+             (lambda: B.w8a8_gemm_splitk(xq, sx, w, sw, S, residual=r, y=y, workspace=ws))
+        for _ in range(3):
+            fn()
+        t = Timer(torch)
+        for _ in range(30):
+            t.run("g", fn)
+        torch.cuda.synchronize()
+        us = t.mean_us("g")
+        ops = 2.0 * M * N * K
+        nbytes = M * K + N * K + 4 * (M + N) + 4 * M * N * (2 if res else 1)
+        roof_us = max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+        out[name] = {"shape": [M, N, K], "splitk": S, "us": round(us, 1), "pct_us": t.pct_us("g"),
+                     "TOPS": round(ops / (us * 1e-6) / 1e12, 1),
+                     "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "roof_us": round(roof_us, 1), "frac_of_roof": round(roof_us / us, 4),
+                     "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > ops / (PEAK_INT8_TOPS * 1e12)
+                     else "mfma"}
+        del xq, w, r, y, ws
+    return out
 
 
 def main():
@@ -204,6 +254,7 @@ def main():
     ops_step = 2.0 * M * (N1 * K1 + N2 * K2) + 2.0 * cand1.size * K1
     value = ops_step / (wall / args.steps) / 1e12
     kernels = {k: round(timer.mean_us(k), 2) for k in timer.pairs}
+    kernels_pct = {k: timer.pct_us(k) for k in timer.pairs}
 
     # dominant kernel roofline: gate+up GEMM on the int8 MFMA peak
     gu_us = timer.mean_us("gemm_gate_up")
@@ -256,6 +307,24 @@ def main():
                "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
                "candidate_readout_us": kernels.get("readout_candidates")}
 
+    # streaming read of 4 GiB: the read bandwidth HBM sustains on this GPU
+    rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    rsink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    B.w8a8_probe_stream_read(rbuf, rsink)
+    best_read = 0.0
+    for _ in range(5):
+        t = Timer(torch)
+        nbytes = t.run("r", lambda: B.w8a8_probe_stream_read(rbuf, rsink))
+        torch.cuda.synchronize()
+        best_read = max(best_read, nbytes / (t.mean_us("r") * 1e-6) / 1e9)
+    del rbuf
+    readout["stream_read_GBs"] = round(best_read, 1)
+    readout["frac_of_stream_read"] = round(full_gbs / best_read, 4)
+    for q in quant.values():
+        q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
+
+    mid_m = mid_m_shapes(torch, B, best_read)
+
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
     ceiling = {}
@@ -286,7 +355,7 @@ def main():
                    "candidates": int(cand1.shape[1]), "answer_rows": 1},
         "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
-        "mfma_ceiling": ceiling,
+        "kernels_us_pct": kernels_pct, "mfma_ceiling": ceiling, "mid_m": mid_m,
     }
     print(json.dumps(line), flush=True)
 

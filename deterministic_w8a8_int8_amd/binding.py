@@ -35,6 +35,7 @@ SIGNATURES = {
     "w8a8_abi_version": (_I32, []),
     "w8a8_set_tile_override": (_I32, [_I32]),
     "w8a8_probe_mfma_ceiling": (_I32, [_I32, _I64, _I64, _P, _P, _P]),
+    "w8a8_probe_stream_read": (_I32, [_P, _I64, _P, _P]),
     "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "w8a8_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
@@ -83,6 +84,16 @@ def w8a8_probe_mfma_ceiling(operand_kind, blocks, iters, sink, stream=None) -> i
     _check(_lib.w8a8_probe_mfma_ceiling(int(operand_kind), int(blocks), int(iters), _ptr(sink),
                                         ctypes.byref(ops), _stream(stream)), "w8a8_probe_mfma_ceiling")
     return ops.value
+
+
+def w8a8_probe_stream_read(buf, sink, stream=None) -> int:
+    """Launch the streaming-read diagnostic over all of `buf` (a device
+    tensor); returns the bytes read."""
+    n = buf.numel() * buf.element_size()
+    n -= n % 16
+    _check(_lib.w8a8_probe_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)),
+           "w8a8_probe_stream_read")
+    return n
 
 
 def _check(rc: int, what: str) -> None:

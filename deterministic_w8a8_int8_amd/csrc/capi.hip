@@ -88,6 +88,12 @@ int w8a8_set_tile_override(int kind) {
     return W8A8_OK;
 }
 
+int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* stream) {
+    if (!buf || !aligned(buf, 16) || bytes <= 0 || (bytes & 15) || !sink || !aligned(sink, 4))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
                             int64_t* ops, void* stream) {
     if ((operand_kind != 0 && operand_kind != 1) || blocks <= 0 || blocks > kMaxDim || iters <= 0 ||

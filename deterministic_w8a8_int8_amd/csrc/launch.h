@@ -82,8 +82,9 @@ struct SkinnyArgs {
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
-// Diagnostic MFMA-only kernel (mfma_ceiling.hip).
+// Diagnostic kernels (probes.hip): MFMA-only ceiling and streaming read.
 int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream);
 hipError_t launch_mfma_ceiling(int kind, int64_t blocks, int64_t iters, int32_t* sink,
                                hipStream_t stream);
 

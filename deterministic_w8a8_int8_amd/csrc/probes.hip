@@ -1,4 +1,5 @@
-// Diagnostic: sustained int8 MFMA throughput with no memory traffic.
+// Diagnostics: sustained int8 MFMA throughput with no memory traffic, and
+// a plain streaming read of device memory.
 //
 // The int8 matrix cores of MI355X do not sustain their nominal rate on
 // every operand stream.  With zero or constant operands they run near the
@@ -16,6 +17,8 @@
 //   1  A shaped like per-token-quantised activations (mostly 0 and +-1, a few
 //      large outlier values), B uniform
 // The operands come from an integer hash of the thread and slot numbers.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -84,7 +87,37 @@ __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sin
     if (x == 0x7a5c3e1f) sink[0] = x;
 }
 
+// Streaming read: every thread xors four independent 16-byte nontemporal
+// loads per iteration over a grid-stride loop, so the HBM read path is the
+// only limit.  The sink is written only if the xor equals a fixed constant.
+constexpr int READ_THREADS = 256;
+
+__global__ __launch_bounds__(READ_THREADS) void stream_read_kernel(const i32x4* __restrict__ p,
+                                                                   int64_t n16, int32_t* sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * READ_THREADS;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * READ_THREADS + threadIdx.x;
+    i32x4 acc = {0, 0, 0, 0};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const i32x4 v0 = __builtin_nontemporal_load(p + i);
+        const i32x4 v1 = __builtin_nontemporal_load(p + i + stride);
+        const i32x4 v2 = __builtin_nontemporal_load(p + i + 2 * stride);
+        const i32x4 v3 = __builtin_nontemporal_load(p + i + 3 * stride);
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    const int32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x7a5c3e1f) sink[0] = x;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream) {
+    const int64_t n16 = bytes / 16;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + READ_THREADS - 1) / READ_THREADS, 256 * 8));
+    hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(READ_THREADS), 0,
+                       stream, static_cast<const i32x4*>(buf), n16, sink);
+    return hipGetLastError();
+}
 
 int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters) {
     // per iteration and wave: 32 MFMAs of 32*32*32 multiply-adds (2 ops each)
