@@ -403,6 +403,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 const Frags& cur = f[s & 1];
                 Frags& nxt = f[(s + 1) & 1];
                 int q = 0;   // next-sub-step fragments issued so far
+                // Waves w and w + NW/2 share a SIMD and its matrix pipe.  The
+                // arbiter favours the older wave, which would run its whole
+                // stage first and leave the younger one to finish alone (a
+                // lone wave cannot keep the pipe full) while it waits at the
+                // barrier.  Taking turns at priority, the younger wave in the
+                // first half of the stage and the older in the second, keeps
+                // the two in step.
+                if ((s < C::SUBSTEPS / 2) == (wave >= C::NW / 2)) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
     #pragma unroll
                 for (int i = 0; i < WTM; ++i) {
     #pragma unroll
@@ -419,6 +429,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             while (d < C::LPS) issue_one(fs, d++);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     mfma_drain();
     wait_fills();
 
