@@ -126,7 +126,8 @@ def cpu_baseline(gu, dn, head, cand, seconds):
         xq, sx = oracle.quantize_act(dn["x"][:R], dn["smooth"])
         y = oracle.gemm(xq, sx, dn["w"], dn["sw"], dn["r"][:R])
         xq, sx = oracle.quantize_act(y[-1:], head["smooth"])
-        oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
+        logits, _ = oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
+        oracle.candidate_softmax(logits)
         return time.perf_counter() - t0
 
     threads = oracle.num_threads()
@@ -222,6 +223,7 @@ def main():
     xq3 = torch.empty((1, K1), dtype=torch.int8, device="cuda")
     sx3 = torch.empty((1,), dtype=torch.float32, device="cuda")
     logits = torch.empty((1, cand1.shape[1]), dtype=torch.float32, device="cuda")
+    probs = torch.empty((1, cand1.shape[1]), dtype=torch.float64, device="cuda")
     ws = B.splitk_workspace(M, N2, K2, S) if S > 1 else None
     timer = Timer(torch)
 
@@ -234,9 +236,9 @@ def main():
                                                               workspace=ws))
         else:
             timer.run("gemm_down", lambda: B.w8a8_gemm(xq2, sx2, w2, sw2, residual=r2, y=y2))
-        timer.run("quantize_answer", lambda: B.w8a8_quantize_act(y2, sh, row_idx=answer, xq=xq3, sx=sx3))
-        timer.run("readout_candidates",
-                  lambda: B.w8a8_readout_candidates(xq3, sx3, wh, swh, cand_d, logits=logits))
+        timer.run("answer_head",
+                  lambda: B.w8a8_answer_head(y2, answer, sh, wh, swh, cand_d, xq=xq3, sx=sx3,
+                                             logits=logits, probs=probs))
 
     print("# warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -305,7 +307,7 @@ def main():
                "frac": round(full_gbs / PEAK_HBM_GBS, 4), "us": round(full_us, 1),
                "shape": [int(Mr), head["N"], head["K"]], "kernel": "gemm_skinny",
                "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
-               "candidate_readout_us": kernels.get("readout_candidates")}
+               "answer_head_us": kernels.get("answer_head")}
 
     # streaming read of 4 GiB: the read bandwidth HBM sustains on this GPU
     rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")

@@ -41,6 +41,9 @@ SIGNATURES = {
     "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
     "w8a8_gemm_splitk": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
     "w8a8_readout_candidates": (_I32, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P]),
+    "w8a8_candidate_softmax": (_I32, [_P, _I64, _I64, _P, _P]),
+    "w8a8_answer_head": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _P,
+                                _P, _P, _P, _P]),
 }
 
 
@@ -216,3 +219,46 @@ def w8a8_readout_candidates(xq, sx, w_vocab, sw_vocab, cand, logits=None, err_fl
                                         _ptr(cand), C, _ptr(logits), _ptr(err_flag), _stream(stream)),
            "w8a8_readout_candidates")
     return logits
+
+
+def w8a8_candidate_softmax(logits, probs=None, stream=None):
+    """Binary64 probabilities [M, C] over each row's candidates."""
+    _want(logits, torch.float32, "logits")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [M, C] tensor")
+    M, C = logits.shape
+    if probs is None:
+        probs = torch.empty((M, C), dtype=torch.float64, device=logits.device)
+    _want(probs, torch.float64, "probs")
+    _check(_lib.w8a8_candidate_softmax(_ptr(logits), M, C, _ptr(probs), _stream(stream)),
+           "w8a8_candidate_softmax")
+    return probs
+
+
+def w8a8_answer_head(h, answer_rows, smooth, w_vocab, sw_vocab, cand, xq=None, sx=None,
+                     logits=None, probs=None, err_flag=None, stream=None):
+    """Gather, quantise, candidate logits and candidate softmax of the
+    answer rows of h [rows, K].  Returns (logits fp32 [M, C], probs fp64 [M, C])."""
+    _want(h, torch.float32, "h")
+    _want(answer_rows, torch.int32, "answer_rows")
+    _want(smooth, torch.float32, "smooth")
+    _want(w_vocab, torch.int8, "w_vocab")
+    _want(sw_vocab, torch.float32, "sw_vocab")
+    _want(cand, torch.int32, "cand")
+    if h.dim() != 2 or h.stride(1) != 1:
+        raise ValueError("h must be 2-D with unit column stride")
+    rows, K = h.shape
+    M = answer_rows.numel()
+    C = cand.shape[1] if cand.dim() == 2 else 0
+    if cand.shape[0] != M or not cand.is_contiguous() or not w_vocab.is_contiguous():
+        raise ValueError("cand must be a contiguous [M, C] tensor and w_vocab contiguous")
+    dev = h.device
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev) if xq is None else xq
+    sx = torch.empty((M,), dtype=torch.float32, device=dev) if sx is None else sx
+    logits = torch.empty((M, C), dtype=torch.float32, device=dev) if logits is None else logits
+    probs = torch.empty((M, C), dtype=torch.float64, device=dev) if probs is None else probs
+    _check(_lib.w8a8_answer_head(_ptr(h), h.stride(0), rows, _ptr(answer_rows), M, _ptr(smooth), K,
+                                 _ptr(w_vocab), _ptr(sw_vocab), w_vocab.shape[0], _ptr(cand), C,
+                                 _ptr(xq), _ptr(sx), _ptr(logits), _ptr(probs), _ptr(err_flag),
+                                 _stream(stream)), "w8a8_answer_head")
+    return logits, probs

@@ -33,6 +33,29 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
     return a < b + m && b < a + n;
 }
 
+int check_quantize_args(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                        const float* smooth, int64_t M, int64_t K, const int8_t* xq, const float* sx) {
+    if (M < 0 || x_rows < 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (M > kMaxDim) return W8A8_ERR_SHAPE;
+    if (ldx < K || (ldx % 4) != 0) return W8A8_ERR_INVALID_ARG;
+    if (!row_idx && M > x_rows) return W8A8_ERR_SHAPE;
+    if (M == 0) return W8A8_OK;
+    if (!x || !smooth || !xq || !sx) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(smooth, 16) || !aligned(xq, 16) || !aligned(sx, 4))
+        return W8A8_ERR_ALIGN;
+    if (row_idx && !aligned(row_idx, 4)) return W8A8_ERR_ALIGN;
+    return W8A8_OK;
+}
+
+int check_readout_args(const int8_t* xq, const float* sx, int64_t M, int64_t K, const int8_t* w_vocab,
+                       const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C,
+                       const float* logits, const int32_t* err_flag);
+int run_readout(const int8_t* xq, const float* sx, int64_t M, int64_t K, const int8_t* w_vocab,
+                const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C, float* logits,
+                int32_t* err_flag, hipStream_t s);
+int check_softmax_args(const float* logits, int64_t M, int64_t C, const double* probs);
+
 int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
                     const float* residual, float* y, int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0) return W8A8_ERR_INVALID_ARG;
@@ -107,16 +130,8 @@ int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int
 int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
                       const float* smooth, int64_t M, int64_t K, int8_t* xq, float* sx,
                       void* stream) {
-    if (M < 0 || x_rows < 0) return W8A8_ERR_INVALID_ARG;
-    if (const int kc = check_k(K)) return kc;
-    if (M > kMaxDim) return W8A8_ERR_SHAPE;
-    if (ldx < K || (ldx % 4) != 0) return W8A8_ERR_INVALID_ARG;
-    if (!row_idx && M > x_rows) return W8A8_ERR_SHAPE;
+    if (const int rc = check_quantize_args(x, ldx, x_rows, row_idx, smooth, M, K, xq, sx)) return rc;
     if (M == 0) return W8A8_OK;
-    if (!x || !smooth || !xq || !sx) return W8A8_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(smooth, 16) || !aligned(xq, 16) || !aligned(sx, 4))
-        return W8A8_ERR_ALIGN;
-    if (row_idx && !aligned(row_idx, 4)) return W8A8_ERR_ALIGN;
     const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx};
     return hip_status(w8a8::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
@@ -154,6 +169,44 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
                             const int8_t* w_vocab, const float* sw_vocab, int64_t V,
                             const int32_t* cand, int64_t C, float* logits, int32_t* err_flag,
                             void* stream) {
+    if (const int rc = check_readout_args(xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag))
+        return rc;
+    if (M == 0 || C == 0) return W8A8_OK;
+    return run_readout(xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag,
+                       static_cast<hipStream_t>(stream));
+}
+
+int w8a8_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs, void* stream) {
+    if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
+    return hip_status(w8a8::launch_candidate_softmax(logits, M, C, probs, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_answer_head(const float* h, int64_t ldh, int64_t h_rows, const int32_t* answer_rows,
+                     int64_t M, const float* smooth, int64_t K, const int8_t* w_vocab,
+                     const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C, int8_t* xq,
+                     float* sx, float* logits, double* probs, int32_t* err_flag, void* stream) {
+    if (!answer_rows && M > 0) return W8A8_ERR_INVALID_ARG;
+    if (const int rc = check_quantize_args(h, ldh, h_rows, answer_rows, smooth, M, K, xq, sx)) return rc;
+    if (const int rc = check_readout_args(xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag))
+        return rc;
+    if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
+    if (M == 0) return W8A8_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const w8a8::QuantArgs q{h, ldh, h_rows, answer_rows, smooth, M, K, xq, sx};
+    if (const int rc = hip_status(w8a8::launch_quantize(q, s))) return rc;
+    if (C == 0) return W8A8_OK;
+    if (const int rc = run_readout(xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag, s))
+        return rc;
+    return hip_status(w8a8::launch_candidate_softmax(logits, M, C, probs, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_readout_args(const int8_t* xq, const float* sx, int64_t M, int64_t K, const int8_t* w_vocab,
+                       const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C,
+                       const float* logits, const int32_t* err_flag) {
     if (M < 0 || C < 0 || V <= 0) return W8A8_ERR_INVALID_ARG;
     if (const int kc = check_k(K)) return kc;
     if (C > W8A8_MAX_CANDIDATES) return W8A8_ERR_TOO_MANY_CANDIDATES;
@@ -164,7 +217,12 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
         !aligned(cand, 4) || !aligned(logits, 4))
         return W8A8_ERR_ALIGN;
     if (err_flag && !aligned(err_flag, 4)) return W8A8_ERR_ALIGN;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return W8A8_OK;
+}
+
+int run_readout(const int8_t* xq, const float* sx, int64_t M, int64_t K, const int8_t* w_vocab,
+                const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C, float* logits,
+                int32_t* err_flag, hipStream_t s) {
     // 64 answer rows per launch; each launch gathers M_chunk * C weight rows.
     for (int64_t m0 = 0; m0 < M; m0 += w8a8::SKINNY_MAX_M) {
         const int64_t mc = (M - m0 < w8a8::SKINNY_MAX_M) ? (M - m0) : w8a8::SKINNY_MAX_M;
@@ -175,4 +233,18 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
     return W8A8_OK;
 }
 
-}  // extern "C"
+int check_softmax_args(const float* logits, int64_t M, int64_t C, const double* probs) {
+    if (M < 0 || C < 0) return W8A8_ERR_INVALID_ARG;
+    if (C > W8A8_MAX_CANDIDATES) return W8A8_ERR_TOO_MANY_CANDIDATES;
+    if (M > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M == 0 || C == 0) return W8A8_OK;
+    if (!logits || !probs) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(probs, 8)) return W8A8_ERR_ALIGN;
+    // the read-out writes logits while the softmax reads them: no overlap
+    // with the probabilities
+    if (overlaps(logits, static_cast<size_t>(M * C) * 4, probs, static_cast<size_t>(M * C) * 8))
+        return W8A8_ERR_INVALID_ARG;
+    return W8A8_OK;
+}
+
+}  // namespace

@@ -82,6 +82,11 @@ struct SkinnyArgs {
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
+// Candidate softmax in binary64, one fixed operation sequence (softmax.hip):
+// probs[m, c] for c < C <= 64; rows with a non-finite logit give NaN.
+hipError_t launch_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs,
+                                    hipStream_t stream);
+
 // Diagnostic kernels (probes.hip): MFMA-only ceiling and streaming read.
 int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream);

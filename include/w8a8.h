@@ -222,6 +222,51 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
                             const int32_t* cand, int64_t C, float* logits, int32_t* err_flag,
                             void* stream);
 
+/*
+ * w8a8_candidate_softmax -- the probabilities over each row's candidates.
+ * The dsiab.com post, section "方案", normalises the candidate scores
+ * within the candidate set (equal to the full-vocabulary softmax
+ * renormalised over the candidates); the review page says the decision
+ * model returns probabilities for the options.  One fixed sequence of
+ * binary64 operations, identical on every run and for any batch:
+ *     mx = max_c (double)logits[m,c];  e_c = exp(logits[m,c] - mx)
+ *     S  = (((e_0 + e_1) + e_2) + ...) + e_{C-1}   (candidate order)
+ *     probs[m,c] = e_c / S
+ * exp is the library's own (Cody-Waite reduction, degree-13 Taylor
+ * polynomial with fused multiply-adds); the relative error of a
+ * probability is at most about (C + 6) binary64 units in the last place.
+ * A row with a non-finite logit (NaN from a bad candidate id) gets NaN for
+ * every candidate.
+ *
+ * logits   device fp32 [M,C], 4-byte aligned.
+ * probs    device fp64 [M,C], 8-byte aligned, not overlapping logits.
+ * C        0 <= C <= W8A8_MAX_CANDIDATES (else W8A8_ERR_TOO_MANY_CANDIDATES).
+ */
+int w8a8_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs, void* stream);
+
+/*
+ * w8a8_answer_head -- the answer read-out end to end, in three launches on
+ * `stream`: w8a8_quantize_act of the hidden rows answer_rows[0..M) of h
+ * (the answer positions; review page, section "Compute shared evidence
+ * once"), w8a8_readout_candidates on them, and w8a8_candidate_softmax.
+ * Every result is bit-identical to calling those three entry points in
+ * turn with the same arguments.  All arguments are checked before the first
+ * launch; a rejected call writes nothing.
+ *
+ * h, ldh, h_rows   device fp32 hidden states [h_rows, ldh] (as x of
+ *                  w8a8_quantize_act); answer_rows device int32 [M], required.
+ * smooth, K        the lm_head's smoothing vector [K] (as in w8a8_quantize_act).
+ * w_vocab, sw_vocab, V, cand, C, err_flag   as in w8a8_readout_candidates.
+ * xq, sx           device scratch owned by the caller: int8 [M,K] (16-byte
+ *                  aligned) and fp32 [M]; they hold the quantised rows after
+ *                  the call.
+ * logits           device fp32 [M,C]; probs device fp64 [M,C].
+ */
+int w8a8_answer_head(const float* h, int64_t ldh, int64_t h_rows, const int32_t* answer_rows,
+                     int64_t M, const float* smooth, int64_t K, const int8_t* w_vocab,
+                     const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C, int8_t* xq,
+                     float* sx, float* logits, double* probs, int32_t* err_flag, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

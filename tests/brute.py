@@ -98,3 +98,19 @@ def epilogue(acc: int, sx, sw, r=None) -> float:
     if r is None:
         return t2
     return round_f32(Fraction(t2) + f32(r))
+
+
+def softmax_decimal(row, digits=40):
+    """Softmax of one row of binary32 logits, computed in decimal arithmetic
+    with ``digits`` significant digits (``Decimal.exp`` rounds correctly at
+    that precision), then rounded to binary64.  A reference far more accurate
+    than any binary64 implementation, for bounding one in units in the last
+    place."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits
+        z = [Decimal(float(v)) for v in row]        # binary32 -> exact decimal
+        mx = max(z)
+        e = [(v - mx).exp() for v in z]
+        s = sum(e, Decimal(0))
+        return [float(v / s) for v in e]

@@ -109,6 +109,21 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 65, p, nul, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 0, p, 4, p, nul, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 0, p, nul, S) == B.W8A8_OK
+    # candidate softmax
+    assert lib.w8a8_candidate_softmax(p, 3, 65, p, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
+    assert lib.w8a8_candidate_softmax(p, -1, 4, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_candidate_softmax(nul, 3, 4, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_candidate_softmax(p, 3, 4, ctypes.c_void_p(p.value + 4), S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_candidate_softmax(p, 3, 4, ctypes.c_void_p(p.value + 8), S) == B.W8A8_ERR_INVALID_ARG  # overlap
+    assert lib.w8a8_candidate_softmax(p, 0, 4, p, S) == B.W8A8_OK
+    # answer head: every stage's checks run before the first launch
+    q = ctypes.c_void_p(p.value + 4096)
+    assert lib.w8a8_answer_head(p, 64, 8, nul, 3, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 96, p, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 64, p, p, 10, p, 65, p, p, p, q, nul, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
+    assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 64, odd, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 64, p, p, 10, p, 4, p, p, p, odd, nul, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_answer_head(p, 64, 8, p, 0, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_OK
     assert lib.w8a8_set_tile_override(99) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_set_tile_override(-2) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_mfma_ceiling(2, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
