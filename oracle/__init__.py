@@ -60,8 +60,12 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_gemm_sampled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i64, p, p, i64, p]
     L.oracle_gemm_acc.argtypes = [p, p, i64, i64, i64, i32, i64, p]
     L.oracle_readout_candidates.argtypes = [p, p, i64, i64, p, p, i64, p, i64, p, p]
+    L.oracle_row_absmax.argtypes = [p, i64, p, p, i64, i64, p]
+    L.oracle_quantize_act_amax.argtypes = [p, i64, p, p, p, i64, i64, p, p]
+    L.oracle_epilogue_acc.argtypes = [p, p, p, p, p, i64, i64]
     for f in ("oracle_quantize_act", "oracle_gemm", "oracle_gemm_sampled", "oracle_gemm_acc",
-              "oracle_readout_candidates", "oracle_num_threads"):
+              "oracle_readout_candidates", "oracle_num_threads", "oracle_row_absmax",
+              "oracle_quantize_act_amax", "oracle_epilogue_acc"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -121,6 +125,55 @@ def quantize_act(x, smooth, row_idx=None):
     _check(lib().oracle_quantize_act(_ptr(x), ldx, _ptr(ri), _ptr(smooth), M, K, _ptr(xq), _ptr(sx)),
            "quantize_act")
     return xq, sx
+
+
+def _rows(x):
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.strides[1] != 4:
+        x = np.ascontiguousarray(x)
+    return x, x.strides[0] // 4
+
+
+def row_absmax(x, smooth, row_idx=None):
+    """max_k |fl(x[m,k] / smooth[k])| per row (the first two quantisation
+    steps on their own, as a rank of a row-parallel layer computes them on
+    its K-slice before the exact MAX across ranks)."""
+    x, ldx = _rows(x)
+    smooth = _c(smooth, np.float32)
+    ri = None if row_idx is None else _c(row_idx, np.int32)
+    M = x.shape[0] if ri is None else ri.shape[0]
+    amax = np.empty((M,), dtype=np.float32)
+    _check(lib().oracle_row_absmax(_ptr(x), ldx, _ptr(ri), _ptr(smooth), M, x.shape[1], _ptr(amax)),
+           "row_absmax")
+    return amax
+
+
+def quantize_act_amax(x, smooth, amax, row_idx=None):
+    """The last two quantisation steps with a given per-token maximum (the
+    global one of a row-parallel layer): returns ``(xq, sx)``."""
+    x, ldx = _rows(x)
+    smooth = _c(smooth, np.float32)
+    amax = _c(amax, np.float32)
+    ri = None if row_idx is None else _c(row_idx, np.int32)
+    M = x.shape[0] if ri is None else ri.shape[0]
+    K = x.shape[1]
+    xq = np.empty((M, K), dtype=np.int8)
+    sx = np.empty((M,), dtype=np.float32)
+    _check(lib().oracle_quantize_act_amax(_ptr(x), ldx, _ptr(ri), _ptr(smooth), _ptr(amax), M, K,
+                                          _ptr(xq), _ptr(sx)), "quantize_act_amax")
+    return xq, sx
+
+
+def epilogue_acc(acc, sx, sw, residual=None):
+    """The fixed binary32 epilogue of given exact accumulators [M,N]."""
+    acc = _c(acc, np.int64)
+    sx, sw = _c(sx, np.float32), _c(sw, np.float32)
+    M, N = acc.shape
+    r = None if residual is None else _c(residual, np.float32)
+    y = np.empty((M, N), dtype=np.float32)
+    _check(lib().oracle_epilogue_acc(_ptr(acc), _ptr(sx), _ptr(sw), _ptr(r), _ptr(y), M, N),
+           "epilogue_acc")
+    return y
 
 
 def gemm(xq, sx, w, sw, residual=None, splitk=1):

@@ -111,6 +111,64 @@ int oracle_quantize_act(const float* x, int64_t ldx, const int32_t* row_idx,
     return ORACLE_OK;
 }
 
+/* Tensor-parallel row-parallel layers (review page, section "Bitwise
+ * consistency is not lossless quantization": tensor parallelism combines
+ * integer partial sums before scaling).  A rank holds a K-slice of the
+ * activations.  For the integer partials of the ranks to be added before
+ * scaling they must share one per-token scale, so the plainest reading is:
+ * each rank takes the maximum of its smoothed slice, the maxima are combined
+ * by an exact MAX across ranks, and every rank quantises its slice with the
+ * token scale of that global maximum.  The two steps of oracle_quantize_act
+ * are therefore also given separately. */
+
+/* Steps 1+2 only: amax[m] = max_k |fl(x[m,k] / smooth[k])| over this slice. */
+int oracle_row_absmax(const float* x, int64_t ldx, const int32_t* row_idx,
+                      const float* smooth, int64_t M, int64_t K, float* amax_out) {
+    if (!x || !smooth || !amax_out || M < 0 || K <= 0 || ldx < K) return ORACLE_ERR_ARG;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const int64_t src = row_idx ? (int64_t)row_idx[m] : m;
+        const float* xr = x + src * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float ab = fabsf(xr[k] / smooth[k]);
+            if (ab > amax) amax = ab;
+        }
+        amax_out[m] = amax;
+    }
+    return ORACLE_OK;
+}
+
+/* Steps 3+4 with a given per-token maximum (the global one): sx = fl(amax/127)
+ * and q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), q = 0 when sx = 0. */
+int oracle_quantize_act_amax(const float* x, int64_t ldx, const int32_t* row_idx,
+                             const float* smooth, const float* amax_in, int64_t M, int64_t K,
+                             int8_t* xq, float* sx) {
+    if (!x || !smooth || !amax_in || !xq || !sx || M < 0 || K <= 0 || ldx < K) return ORACLE_ERR_ARG;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const int64_t src = row_idx ? (int64_t)row_idx[m] : m;
+        const float* xr = x + src * ldx;
+        float s = amax_in[m] / 127.0f;
+        sx[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t q = 0;
+            if (s != 0.0f) {
+                float xs = xr[k] / smooth[k];
+                float t = xs / s;
+                float r = oracle_round_half_even(t);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                q = (int8_t)(int)r;
+            }
+            xq[m * K + k] = q;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Split-K chunk c of S: [c*Kc, min((c+1)*Kc, K)) with Kc = ceil(K/S) rounded
  * up to a multiple of ktile. */
 static void oracle_chunk(int64_t K, int splitk, int64_t ktile, int c, int64_t* k0, int64_t* k1) {
@@ -222,6 +280,23 @@ int oracle_gemm_acc(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int
                 err = ORACLE_ERR_OVERFLOW;
             }
             acc_out[m * N + n] = acc;
+        }
+    }
+    return err;
+}
+
+/* The epilogue of given exact accumulators (the integer partials of the
+ * ranks already added): y[m,n] = epilogue(acc[m,n]).  An accumulator outside
+ * the int32 range is an error. */
+int oracle_epilogue_acc(const int64_t* acc, const float* sx, const float* sw,
+                        const float* residual, float* y, int64_t M, int64_t N) {
+    if (!acc || !sx || !sw || !y || M < 0 || N < 0) return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const int64_t a = acc[m * N + n];
+            if (a > ORACLE_INT32_MAX || a < -ORACLE_INT32_MAX) err = ORACLE_ERR_OVERFLOW;
+            y[m * N + n] = oracle_epilogue(a, sx[m], sw[n], residual ? residual + m * N + n : 0);
         }
     }
     return err;

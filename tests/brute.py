@@ -114,3 +114,20 @@ def softmax_decimal(row, digits=40):
         e = [(v - mx).exp() for v in z]
         s = sum(e, Decimal(0))
         return [float(v / s) for v in e]
+
+
+def quantize_row_amax(x_row, s_row, amax):
+    """Quantisation of one row with a given per-token maximum (the global one
+    of a row-parallel layer), each binary32 step exact then rounded:
+    sx = fl(amax/127); q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), 0 when sx = 0."""
+    sx = round_f32(f32(amax) / 127)
+    q = []
+    for x, s in zip(x_row, s_row):
+        if sx == 0:
+            q.append(0)
+            continue
+        v = round_f32(f32(x) / f32(s))
+        t = Fraction(round_f32(Fraction(v) / Fraction(sx)))
+        r = _round_half_even_int(abs(t)) * (1 if t >= 0 else -1)
+        q.append(max(-127, min(127, r)))
+    return q, sx
