@@ -142,6 +142,45 @@ def cpu_baseline(gu, dn, head, cand, seconds):
                       f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
 
 
+def row_parallel_rank(torch, B, x2, s2, w2, sw2, r2):
+    """One rank's kernels of the row-parallel down projection (8192 x 5120 x
+    17408 split over `ranks`), each timed alone: the slice maximum, the
+    quantisation with the global maximum, the int32 partial GEMM of the
+    slice, and the epilogue that adds all ranks' partials (what follows the
+    int32 all-reduce)."""
+    M, K = x2.shape
+    N = w2.shape[0]
+    out = {}
+    for ranks in (2, 8):
+        ks = K // ranks
+        xs, ss = x2[:, :ks], s2[:ks]
+        ws = w2[:, :ks].contiguous()
+        amax = B.w8a8_row_absmax(xs, ss)
+        xq, sx = B.w8a8_quantize_act_amax(xs, ss, amax)
+        parts = torch.empty((ranks, M, N), dtype=torch.int32, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        fns = {"row_absmax": lambda: B.w8a8_row_absmax(xs, ss, amax=amax),
+               "quantize_act_amax": lambda: B.w8a8_quantize_act_amax(xs, ss, amax, xq=xq, sx=sx),
+               "gemm_int32": lambda: B.w8a8_gemm_int32(xq, ws, acc=parts[0]),
+               "epilogue_int32": lambda: B.w8a8_epilogue_int32(parts, sx, sw2, residual=r2, y=y)}
+        res = {}
+        for name, fn in fns.items():
+            for _ in range(2):
+                fn()
+            t = Timer(torch)
+            for _ in range(10):
+                t.run(name, fn)
+            torch.cuda.synchronize()
+            res[name] = {"us": round(t.mean_us(name), 1)}
+        res["row_absmax"]["GBs"] = round(4 * M * ks / (res["row_absmax"]["us"] * 1e-6) / 1e9, 1)
+        res["quantize_act_amax"]["GBs"] = round(5 * M * ks / (res["quantize_act_amax"]["us"] * 1e-6) / 1e9, 1)
+        res["gemm_int32"]["TOPS"] = round(2.0 * M * N * ks / (res["gemm_int32"]["us"] * 1e-6) / 1e12, 1)
+        res["epilogue_int32"]["GBs"] = round((4 * ranks + 8) * M * N / (res["epilogue_int32"]["us"] * 1e-6) / 1e9, 1)
+        out[f"{ranks}_ranks"] = {"slice_K": ks, **res}
+        del parts, y, ws
+    return out
+
+
 def mid_m_shapes(torch, B, stream_read_gbs):
     """The short-request (M = 256) and forest-batch (M = 328) projections:
     near the ridge of the int8 roofline, so each reports its time against
@@ -326,6 +365,7 @@ def main():
         q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
 
     mid_m = mid_m_shapes(torch, B, best_read)
+    row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2)
 
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
@@ -358,6 +398,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
         "kernels_us_pct": kernels_pct, "mfma_ceiling": ceiling, "mid_m": mid_m,
+        "row_parallel_rank": row_parallel,
     }
     print(json.dumps(line), flush=True)
 

@@ -42,6 +42,10 @@ SIGNATURES = {
     "w8a8_gemm_splitk": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
     "w8a8_readout_candidates": (_I32, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P]),
     "w8a8_candidate_softmax": (_I32, [_P, _I64, _I64, _P, _P]),
+    "w8a8_row_absmax": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _P]),
+    "w8a8_quantize_act_amax": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P]),
+    "w8a8_gemm_int32": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
+    "w8a8_epilogue_int32": (_I32, [_P, _I32, _P, _P, _P, _P, _I64, _I64, _P]),
     "w8a8_answer_head": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _P, _P,
                                 _P, _P, _P, _P]),
 }
@@ -219,6 +223,72 @@ def w8a8_readout_candidates(xq, sx, w_vocab, sw_vocab, cand, logits=None, err_fl
                                         _ptr(cand), C, _ptr(logits), _ptr(err_flag), _stream(stream)),
            "w8a8_readout_candidates")
     return logits
+
+
+def w8a8_row_absmax(x, smooth, row_idx=None, amax=None, accumulate=False, stream=None):
+    """Exact per-row maximum of the smoothed slice x [rows, K]; with
+    ``accumulate`` it is max-combined into ``amax``."""
+    _want(x, torch.float32, "x")
+    _want(smooth, torch.float32, "smooth")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, K = x.shape
+    M = row_idx.numel() if row_idx is not None else rows
+    if amax is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing amax")
+        amax = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _want(amax, torch.float32, "amax")
+    _check(_lib.w8a8_row_absmax(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth), M, K,
+                                1 if accumulate else 0, _ptr(amax), _stream(stream)), "w8a8_row_absmax")
+    return amax
+
+
+def w8a8_quantize_act_amax(x, smooth, amax, row_idx=None, xq=None, sx=None, stream=None):
+    """Per-token quantisation with the given per-token maxima amax [M]."""
+    _want(x, torch.float32, "x")
+    _want(smooth, torch.float32, "smooth")
+    _want(amax, torch.float32, "amax")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, K = x.shape
+    M = row_idx.numel() if row_idx is not None else rows
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device) if sx is None else sx
+    _check(_lib.w8a8_quantize_act_amax(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth),
+                                       _ptr(amax), M, K, _ptr(xq), _ptr(sx), _stream(stream)),
+           "w8a8_quantize_act_amax")
+    return xq, sx
+
+
+def w8a8_gemm_int32(xq, w, acc=None, stream=None):
+    """Exact int32 accumulators [M, N] of xq [M, K] and w [N, K]."""
+    for t, n in ((xq, "xq"), (w, "w")):
+        _want(t, torch.int8, n)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K]")
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if acc is None else acc
+    _want(acc, torch.int32, "acc")
+    _check(_lib.w8a8_gemm_int32(_ptr(xq), _ptr(w), M, N, K, _ptr(acc), _stream(stream)), "w8a8_gemm_int32")
+    return acc
+
+
+def w8a8_epilogue_int32(parts, sx, sw, residual=None, y=None, stream=None):
+    """y = epilogue(sum over the S slices of parts [S, M, N] int32, in order)."""
+    _want(parts, torch.int32, "parts")
+    if parts.dim() == 2:
+        parts = parts.unsqueeze(0)
+    if parts.dim() != 3 or not parts.is_contiguous():
+        raise ValueError("parts must be a contiguous [S, M, N] tensor")
+    S, M, N = parts.shape
+    y = torch.empty((M, N), dtype=torch.float32, device=parts.device) if y is None else y
+    _check(_lib.w8a8_epilogue_int32(_ptr(parts), S, _ptr(sx), _ptr(sw), _ptr(residual), _ptr(y), M, N,
+                                    _stream(stream)), "w8a8_epilogue_int32")
+    return y
 
 
 def w8a8_candidate_softmax(logits, probs=None, stream=None):

@@ -81,7 +81,7 @@ int run_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw
         return hip_status(w8a8::launch_skinny(s, stream));
     }
     const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
-    const GemmArgs a{xq, sx, w, sw, residual, y, M, N, K};
+    const GemmArgs a{xq, sx, w, sw, residual, y, M, N, K, nullptr};
     return hip_status(w8a8::launch_gemm_tiled(a, plan, workspace, stream));
 }
 
@@ -132,7 +132,7 @@ int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t
                       void* stream) {
     if (const int rc = check_quantize_args(x, ldx, x_rows, row_idx, smooth, M, K, xq, sx)) return rc;
     if (M == 0) return W8A8_OK;
-    const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx};
+    const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx, nullptr};
     return hip_status(w8a8::launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -176,6 +176,60 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
                        static_cast<hipStream_t>(stream));
 }
 
+int w8a8_row_absmax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                    const float* smooth, int64_t M, int64_t K, int accumulate, float* amax,
+                    void* stream) {
+    if (!amax && M > 0) return W8A8_ERR_INVALID_ARG;
+    // the same checks as quantisation, with amax standing in for xq and sx
+    if (const int rc = check_quantize_args(x, ldx, x_rows, row_idx, smooth, M, K,
+                                           reinterpret_cast<const int8_t*>(x), amax))
+        return rc;
+    if (M == 0) return W8A8_OK;
+    const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, nullptr, nullptr, nullptr};
+    return hip_status(w8a8::launch_row_absmax(a, accumulate != 0, amax, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_quantize_act_amax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                           const float* smooth, const float* amax, int64_t M, int64_t K, int8_t* xq,
+                           float* sx, void* stream) {
+    if (const int rc = check_quantize_args(x, ldx, x_rows, row_idx, smooth, M, K, xq, sx)) return rc;
+    if (M == 0) return W8A8_OK;
+    if (!amax) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(amax, 4)) return W8A8_ERR_ALIGN;
+    const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx, amax};
+    return hip_status(w8a8::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_gemm_int32(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int64_t K, int32_t* acc,
+                    void* stream) {
+    if (M < 0 || N < 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (M > kMaxDim || N > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!xq || !w || !acc) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(xq, 16) || !aligned(w, 16) || !aligned(acc, 16)) return W8A8_ERR_ALIGN;
+    const GemmArgs a{xq, nullptr, w, nullptr, nullptr, nullptr, M, N, K, acc};
+    const GemmPlan plan = w8a8::plan_gemm(M, N, K, 1);
+    return hip_status(w8a8::launch_gemm_tiled(a, plan, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_epilogue_int32(const int32_t* parts, int S, const float* sx, const float* sw,
+                        const float* residual, float* y, int64_t M, int64_t N, void* stream) {
+    if (M < 0 || N < 0 || S < 1 || S > W8A8_MAX_SPLITK) return W8A8_ERR_INVALID_ARG;
+    if (M > kMaxDim || N > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W8A8_OK;
+    if (!parts || !sx || !sw || !y) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(parts, 4) || !aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 4)) return W8A8_ERR_ALIGN;
+    const size_t out = static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
+    if (overlaps(parts, out * static_cast<size_t>(S), y, out)) return W8A8_ERR_INVALID_ARG;
+    if (residual) {
+        if (!aligned(residual, 4)) return W8A8_ERR_ALIGN;
+        if (residual != y && overlaps(residual, out, y, out)) return W8A8_ERR_INVALID_ARG;
+    }
+    const GemmArgs a{nullptr, sx, nullptr, sw, residual, y, M, N, 0, nullptr};
+    return hip_status(w8a8::launch_reduce(a, S, parts, static_cast<hipStream_t>(stream)));
+}
+
 int w8a8_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs, void* stream) {
     if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
     return hip_status(w8a8::launch_candidate_softmax(logits, M, C, probs, static_cast<hipStream_t>(stream)));
@@ -192,7 +246,7 @@ int w8a8_answer_head(const float* h, int64_t ldh, int64_t h_rows, const int32_t*
     if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
     if (M == 0) return W8A8_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const w8a8::QuantArgs q{h, ldh, h_rows, answer_rows, smooth, M, K, xq, sx};
+    const w8a8::QuantArgs q{h, ldh, h_rows, answer_rows, smooth, M, K, xq, sx, nullptr};
     if (const int rc = hip_status(w8a8::launch_quantize(q, s))) return rc;
     if (C == 0) return W8A8_OK;
     if (const int rc = run_readout(xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag, s))

@@ -451,13 +451,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int col = col0 + wn * 32 * WTN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                swv[j][e] = sw[min(col, N - 1)];
+                swv[j][e] = part ? 0.0f : sw[min(col, N - 1)];
             }
 #pragma unroll
         for (int i = 0; i < WTM; ++i) {
             const int row = row0 + wm * 32 * WTM + i * 32 + (lane & 31);
             if (row >= M) continue;
-            const float sxm = sx[row];
+            const float sxm = part ? 0.0f : sx[row];
 #pragma unroll
             for (int j = 0; j < WTN; ++j) {
 #pragma unroll
@@ -513,8 +513,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
     float* s_sw = s_sx + C::BM;
     __syncthreads();  // all waves are done reading the operand buffers
-    for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
-    for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
+    if (!part) {   // raw int32 output reads no scales
+        for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
+        for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
+    }
 
     // (a partial slice starts 16-byte aligned whenever N % 4 == 0: the
     // workspace is 256-byte aligned)
@@ -687,11 +689,14 @@ __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce(
     }
 }
 
+}  // namespace
+
 hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipStream_t stream) {
     const int64_t MN = a.M * a.N;
     const bool vec = (a.N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.sw) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(a.residual) & 15) == 0;
+                     (reinterpret_cast<uintptr_t>(a.residual) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(partials) & 15) == 0;
     const int64_t units = vec ? MN / 4 : MN;
     // about 4 units per thread with at most 32 workgroups per CU resident
     const int64_t blocks = std::max<int64_t>(
@@ -707,6 +712,8 @@ hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipS
     return hipGetLastError();
 }
 
+namespace {
+
 // The configurations, indexed by TileKind.
 using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1>;  // 256x256, 4 waves, 128-byte stages x2
 using Cfg1 = Cfg<2, 4, 4, 2, 64, 4, 1>;   // 256x256, 8 waves, 64-byte stages x4
@@ -720,14 +727,14 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hip
     const int64_t ntiles = p.tiles_m * p.tiles_n;
     const int KB = static_cast<int>(a.K >> 6);
     const int kb_per_split = (KB + p.splitk - 1) / p.splitk;
-    int32_t* partials = p.splitk > 1 ? static_cast<int32_t*>(workspace) : nullptr;
+    int32_t* partials = a.acc_out ? a.acc_out : p.splitk > 1 ? static_cast<int32_t*>(workspace) : nullptr;
     const unsigned nblocks = static_cast<unsigned>(ntiles * p.splitk);
     hipLaunchKernelGGL((gemm_tiled<C>), dim3(nblocks), dim3(C::THREADS), 0, stream, a.xq, a.sx, a.w,
                        a.sw, a.residual, a.y, static_cast<int>(a.M), static_cast<int>(a.N),
                        static_cast<int>(a.K), static_cast<int>(p.tiles_m),
                        static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, partials);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splitk <= 1) return e;
+    if (e != hipSuccess || p.splitk <= 1 || a.acc_out) return e;
     return launch_reduce(a, p.splitk, partials, stream);
 }
 

@@ -18,9 +18,13 @@ struct QuantArgs {
     int64_t K;
     int8_t* xq;
     float* sx;
+    const float* amax;   // given per-token maxima [M], or NULL: each row's own
 };
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// amax_out[m] = exact max_k |fl(x/s)| of row m (max-combined with amax_out[m]
+// when accumulate); xq, sx and amax of `a` are unused.
+hipError_t launch_row_absmax(const QuantArgs& a, bool accumulate, float* amax_out, hipStream_t stream);
 
 struct GemmArgs {
     const int8_t* xq;
@@ -32,6 +36,8 @@ struct GemmArgs {
     int64_t M;
     int64_t N;
     int64_t K;
+    int32_t* acc_out;   // non-NULL: write the raw int32 accumulators [M,N] here
+                        // instead of the epilogue (splitk 1; sx, sw, residual, y unused)
 };
 
 // Tiled MFMA GEMM.  Which tile shape runs depends only on (M, N, K, splitk);
@@ -56,6 +62,8 @@ void set_tile_override(int kind);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,
                              hipStream_t stream);
+// y = epilogue(P_0 + ... + P_{S-1}) for S int32 slices [S,M,N] (row-major).
+hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipStream_t stream);
 
 // Skinny-M GEMM (M <= SKINNY_MAX_M): the weight is streamed from HBM once and
 // every wave keeps 16 weight rows against all M activation rows.  With

@@ -126,12 +126,13 @@ __device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d
 }
 
 // NV float4 per thread held in registers: K <= NV * 4 * T; ROWS rows per
-// workgroup of T threads.
-template <int NV, int T, int ROWS>
+// workgroup of T threads.  GIVEN: the per-token maximum comes from amax_in
+// (a row-parallel layer's global maximum) instead of the row itself.
+template <int NV, int T, int ROWS, bool GIVEN>
 __global__ __launch_bounds__(T) void quantize_rows_reg(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
-    float* __restrict__ sx) {
+    float* __restrict__ sx, const float* __restrict__ amax_in) {
     constexpr int NW = T / 64;
     __shared__ float redf[4][NW];
     __shared__ int redi[NW];
@@ -169,19 +170,30 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
         for (int i = 0; i < NV; ++i) {
             const int j = t + i * T;
             xv[i] = j < K4 ? xr[j] : f4(0.0f);
-            const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y, xv[i].z * rv[i].z,
-                                          xv[i].w * rv[i].w);
-            amax_a = absmax4(amax_a, ap);
+            if constexpr (!GIVEN) {
+                const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y,
+                                              xv[i].z * rv[i].z, xv[i].w * rv[i].w);
+                amax_a = absmax4(amax_a, ap);
+            }
         }
         float* red0 = redf[(2 * rr) & 3];
         float* red1 = redf[(2 * rr + 1) & 3];
+        float amax = 0.0f;
+        bool exact_row;
+        bool valid = ok;
+        if constexpr (GIVEN) {
+            // a given maximum: no reduction over the row.  A NaN or negative
+            // one marks the row invalid, like a bad row index.
+            amax = amax_in[m];
+            valid = ok && amax >= 0.0f;
+            exact_row = odd_cols || !(amax >= 0x1p-96f);
+        } else {
         amax_a = block_max<NW>(amax_a, red0);
-        const bool exact_row = odd_cols || !(amax_a >= 0x1p-96f);
+        exact_row = odd_cols || !(amax_a >= 0x1p-96f);
 
         // exact maximum: true divisions for the candidates only (or every
         // element on an exact row)
         const float thresh = amax_a * (1.0f - 0x1p-19f);
-        float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int j = t + i * T;
@@ -200,8 +212,9 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
             }
         }
         amax = block_max<NW>(amax, red1);
-        const float scale = ok ? amax / 127.0f : 0.0f;
-        if (t == 0) sx[m] = ok ? scale : quiet_nan();
+        }
+        const float scale = valid ? amax / 127.0f : 0.0f;
+        if (t == 0) sx[m] = valid ? scale : quiet_nan();
         const float inv = fast_rcp(scale);
 
         uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
@@ -229,10 +242,36 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 
 // Any K: the row is read twice (the second read usually hits L2) and every
 // element takes the exact divisions.
+// Exact max_k |fl(x[m,k]/s[k])| of one row (every element divided).
+__device__ __forceinline__ float row_absmax_exact(const float4* xr, const float4* s4, int64_t K4,
+                                                  float* red) {
+    float amax = 0.0f;
+    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
+        const float4 a = xr[j], s = s4[j];
+        amax = absmax4(amax, make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w));
+    }
+    return block_max<QTHREADS / 64>(amax, red);
+}
+
+// The slice maximum of a row-parallel rank: amax[m] = (max with amax[m] if
+// accumulate) of row m's exact smoothed maximum; NaN for a bad row index.
+__global__ __launch_bounds__(QTHREADS) void row_absmax_kernel(
+    const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
+    const float* __restrict__ smooth, int64_t K, int accumulate, float* __restrict__ amax_out) {
+    __shared__ float red[QTHREADS / 64];
+    const int64_t m = blockIdx.x;
+    int64_t src;
+    const bool ok = source_row(row_idx, m, x_rows, &src);
+    const float a = row_absmax_exact(reinterpret_cast<const float4*>(x + src * ldx),
+                                     reinterpret_cast<const float4*>(smooth), K >> 2, red);
+    if (threadIdx.x == 0) amax_out[m] = !ok ? quiet_nan() : accumulate ? fmaxf(amax_out[m], a) : a;
+}
+
 __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
-    const float* __restrict__ smooth, int64_t K, int8_t* __restrict__ xq, float* __restrict__ sx) {
-    __shared__ float red[4];
+    const float* __restrict__ smooth, int64_t K, int8_t* __restrict__ xq, float* __restrict__ sx,
+    const float* __restrict__ amax_in) {
+    __shared__ float red[QTHREADS / 64];
     const int64_t m = blockIdx.x;
     int64_t src;
     const bool ok = source_row(row_idx, m, x_rows, &src);
@@ -240,14 +279,10 @@ __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
     const int64_t K4 = K >> 2;
 
-    float amax = 0.0f;
-    for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
-        const float4 a = xr[j], s = s4[j];
-        amax = absmax4(amax, make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w));
-    }
-    amax = block_max<QTHREADS / 64>(amax, red);
-    const float scale = ok ? amax / 127.0f : 0.0f;
-    if (threadIdx.x == 0) sx[m] = ok ? scale : quiet_nan();
+    const float amax = amax_in ? amax_in[m] : row_absmax_exact(xr, s4, K4, red);
+    const bool valid = ok && amax >= 0.0f;
+    const float scale = valid ? amax / 127.0f : 0.0f;
+    if (threadIdx.x == 0) sx[m] = valid ? scale : quiet_nan();
 
     uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
     for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
@@ -261,8 +296,14 @@ template <int NV, int T>
 hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
     // One row per workgroup: measured faster than sharing the reciprocals
     // over several rows, because more workgroups keep more rows in flight.
-    hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1>), dim3(static_cast<unsigned>(a.M)), dim3(T), 0,
-                       stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx);
+    if (a.amax)
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, true>), dim3(static_cast<unsigned>(a.M)), dim3(T),
+                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
+                           a.amax);
+    else
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, false>), dim3(static_cast<unsigned>(a.M)), dim3(T),
+                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
+                           nullptr);
     return hipGetLastError();
 }
 
@@ -286,7 +327,14 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     if (n512 <= 12) return launch_reg<12, 512>(a, stream);
     if (n512 <= 16) return launch_reg<16, 512>(a, stream);
     hipLaunchKernelGGL(quantize_rows_stream, dim3(static_cast<unsigned>(a.M)), dim3(QTHREADS), 0,
-                       stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, a.xq, a.sx);
+                       stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, a.xq, a.sx, a.amax);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_absmax(const QuantArgs& a, bool accumulate, float* amax_out, hipStream_t stream) {
+    if (a.M == 0) return hipSuccess;
+    hipLaunchKernelGGL(row_absmax_kernel, dim3(static_cast<unsigned>(a.M)), dim3(QTHREADS), 0, stream,
+                       a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, accumulate ? 1 : 0, amax_out);
     return hipGetLastError();
 }
 

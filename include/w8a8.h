@@ -223,6 +223,63 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
                             void* stream);
 
 /*
+ * Tensor-parallel row-parallel layers.  The review page, section "Bitwise
+ * consistency is not lossless quantization", combines the integer partial
+ * sums of the ranks before scaling.  A rank holds a K-slice of the
+ * activations and of the weight; for its int32 partials to be added before
+ * scaling, every rank quantises with one per-token scale, taken from the
+ * exact MAX of the ranks' slice maxima.  One rank's steps:
+ *   w8a8_row_absmax         slice maximum (then MAX across ranks)
+ *   w8a8_quantize_act_amax  quantise the slice with the global maximum
+ *   w8a8_gemm_int32         int32 partials of the slice (then SUM across ranks)
+ *   w8a8_epilogue_int32     the fixed epilogue of the added partials
+ * With the collectives done exactly (MAX of floats, SUM of int32), the
+ * output is bit-identical to the single-device w8a8_quantize_act + w8a8_gemm
+ * for any number of ranks and any slicing into multiples of 64.
+ */
+
+/*
+ * w8a8_row_absmax -- amax[m] = max_k |fl(x[row m, k] / smooth[k])| over this
+ * K-slice, exact (every element divided).  accumulate != 0: amax[m] =
+ * fmax(amax[m], that value), so successive calls over the slices of one
+ * device give the global maximum.  A row index outside [0, x_rows) writes
+ * NaN.  Arguments as for w8a8_quantize_act; amax device fp32 [M].
+ */
+int w8a8_row_absmax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                    const float* smooth, int64_t M, int64_t K, int accumulate, float* amax,
+                    void* stream);
+
+/*
+ * w8a8_quantize_act_amax -- w8a8_quantize_act with the per-token maximum
+ * given: sx[m] = fl(amax[m] / 127), q = clamp(rne(fl(fl(x/s)/sx)), -127, 127)
+ * (q = 0 when sx = 0).  With amax[m] the row's own maximum this is exactly
+ * w8a8_quantize_act.  amax: device fp32 [M], 4-byte aligned; a NaN or
+ * negative entry (or a bad row index) gives sx = NaN and zero codes.
+ */
+int w8a8_quantize_act_amax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
+                           const float* smooth, const float* amax, int64_t M, int64_t K, int8_t* xq,
+                           float* sx, void* stream);
+
+/*
+ * w8a8_gemm_int32 -- the exact int32 accumulators, no epilogue:
+ *     acc[m,n] = sum_k xq[m,k] * w[n,k]            (row-major [M,N])
+ * xq, w as for w8a8_gemm; acc device int32 [M,N], 16-byte aligned.
+ */
+int w8a8_gemm_int32(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int64_t K, int32_t* acc,
+                    void* stream);
+
+/*
+ * w8a8_epilogue_int32 -- y = epilogue(P_0 + P_1 + ... + P_{S-1}) for S
+ * int32 slices parts [S,M,N] (row-major, slice s at parts + s*M*N), added
+ * in slice order, then the fixed epilogue of w8a8_gemm with sx [M], sw [N]
+ * and the optional residual (may equal y).  The sum must fit int32, which
+ * holds for the partials of one contraction with K <= W8A8_MAX_K.
+ * 1 <= S <= W8A8_MAX_SPLITK; parts must not overlap y.
+ */
+int w8a8_epilogue_int32(const int32_t* parts, int S, const float* sx, const float* sw,
+                        const float* residual, float* y, int64_t M, int64_t N, void* stream);
+
+/*
  * w8a8_candidate_softmax -- the probabilities over each row's candidates.
  * The dsiab.com post, section "方案", normalises the candidate scores
  * within the candidate set (equal to the full-vocabulary softmax

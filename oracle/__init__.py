@@ -106,16 +106,22 @@ def _check(rc, what):
         raise RuntimeError(f"oracle {what} failed with code {rc}")
 
 
+def _rows(x):
+    """Row-strided binary32 view and its row pitch in elements (numpy may
+    report any stride for a dimension of size 1; one row's pitch is K)."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.strides[1] != 4:
+        x = np.ascontiguousarray(x)
+    return x, (x.strides[0] // 4 if x.shape[0] > 1 else x.shape[1])
+
+
 def quantize_act(x, smooth, row_idx=None):
     """Per-token int8 quantisation after the SmoothQuant per-channel divide.
 
     Returns ``(xq int8 [M,K], sx float32 [M])``; with ``row_idx`` the output row
     m is input row ``row_idx[m]``.
     """
-    x = np.asarray(x, dtype=np.float32)
-    if x.ndim != 2 or x.strides[1] != 4:
-        x = np.ascontiguousarray(x)
-    ldx = x.strides[0] // 4
+    x, ldx = _rows(x)
     K = x.shape[1]
     smooth = _c(smooth, np.float32)
     ri = None if row_idx is None else _c(row_idx, np.int32)
@@ -125,13 +131,6 @@ def quantize_act(x, smooth, row_idx=None):
     _check(lib().oracle_quantize_act(_ptr(x), ldx, _ptr(ri), _ptr(smooth), M, K, _ptr(xq), _ptr(sx)),
            "quantize_act")
     return xq, sx
-
-
-def _rows(x):
-    x = np.asarray(x, dtype=np.float32)
-    if x.ndim != 2 or x.strides[1] != 4:
-        x = np.ascontiguousarray(x)
-    return x, x.strides[0] // 4
 
 
 def row_absmax(x, smooth, row_idx=None):

@@ -67,6 +67,53 @@ def test_quantize_ties_and_strides():
     np.testing.assert_array_equal(host(xq)[1, :8], [-127, 0, 2, 2, 4, -2, 126, 0])
 
 
+def _extreme_rows(K, seed):
+    """Rows that leave the fast path's error bounds: smoothing values outside
+    [2^-120, 2^120] (subnormal ones included), subnormal activations, rows
+    whose maximum is tiny, and rows with many equal maxima."""
+    rng = np.random.default_rng(seed)
+    g = lambda: rng.standard_normal(K)
+    rows, smooths = [], []
+    # 1: tiny smoothing values (some subnormal), small activations
+    s = np.exp2(rng.uniform(-140, -110, K))
+    rows.append(g() * 2.0 ** -20); smooths.append(s)
+    # 2: huge smoothing values: smoothed values near 2^-110 (tiny row maximum)
+    s = np.exp2(rng.uniform(100, 126, K))
+    rows.append(g()); smooths.append(s)
+    # 3: huge smoothing values with large activations
+    rows.append(g() * 2.0 ** 100); smooths.append(s)
+    # 4: mixed columns: normal, just below 2^-120 and just above 2^120
+    s = np.where(rng.random(K) < 0.5, rng.uniform(0.5, 4.0, K),
+                 np.where(rng.random(K) < 0.5, np.exp2(rng.uniform(-126, -121, K)),
+                          np.exp2(rng.uniform(121, 126, K))))
+    rows.append(g() * s); smooths.append(s)
+    # 5: subnormal activations with ordinary smoothing
+    s = rng.uniform(0.5, 4.0, K)
+    rows.append(g() * 1e-40); smooths.append(s)
+    # 6: many equal maxima and exact halves
+    x = np.round(g() * 4) / 2
+    x[rng.choice(K, 9, replace=False)] = 63.5
+    rows.append(x); smooths.append(np.ones(K))
+    return [np.asarray(r, np.float32) for r in rows], [np.asarray(v, np.float32) for v in smooths]
+
+
+@pytest.mark.parametrize("K", [1024, 5120, 17408, 40960])
+def test_quantize_extreme_values_match_oracle(K):
+    rows, smooths = _extreme_rows(K, seed=K)
+    for i, (x, s) in enumerate(zip(rows, smooths)):
+        # the row alone and with ordinary rows around it (same smoothing)
+        rng = np.random.default_rng(i)
+        typical = np.float64(np.median(np.abs(x.astype(np.float64) / s)))
+        other = (np.clip(rng.standard_normal(K), -3, 3) * typical * s).astype(np.float32)
+        block = np.stack([x, other, x])
+        with np.errstate(all="ignore"):
+            assert np.isfinite(block).all() and np.isfinite(block / s).all(), "inputs must be finite"
+        xq, sx = B.w8a8_quantize_act(dev(block), dev(s))
+        xq_o, sx_o = oracle.quantize_act(block, s)
+        assert_bits_equal(host(sx), sx_o, f"K={K} case {i + 1} sx")
+        np.testing.assert_array_equal(host(xq), xq_o, err_msg=f"K={K} case {i + 1}")
+
+
 def test_quantize_row_gather_and_bad_index():
     x, s = _quant_case(40, 512, seed=5)
     idx = np.array([39, 0, 17, 17, 5, -1, 40, 2], np.int32)
