@@ -18,20 +18,24 @@
 //     traffic, so the kernel works with reciprocals and proves, per element,
 //     that the cheap value decides the same bits:
 //       * r = rcp(s) (|error| <= 1 ulp) is computed once per column of the
-//         workgroup's row.  x*r is within 2^-22
-//         (relative) of fl(x/s).  The row maximum is found on these
-//         approximations.  Because fl() is monotone, the exact maximum
+//         workgroup's row.  x*r is within 2^-22 (relative) of fl(x/s).
+//         Each wave finds its approximate maximum on these values (shuffles
+//         only).  Because fl() is monotone, the wave's exact maximum
 //         fl(|x_k|/s_k) is reached by an element whose approximation lies
-//         within 2^-19 of the approximate maximum.  Only those few
-//         candidates are divided exactly;
+//         within 2^-19 of that approximate maximum; only those few
+//         candidates are divided exactly.  One block-wide maximum of the
+//         waves' exact maxima is the row's -- a single barrier per row;
 //       * with sx = fl(a/127) (a true division, once per row) and inv =
 //         rcp(sx), t' = (x*r)*inv is within 2^-14 of t = fl(fl(x/s)/sx)
 //         whenever |t| <= 128.  If t' is more than 2^-12 away from every
 //         half-integer, rne(t') = rne(t).  Otherwise (about 5 in 10^4
 //         elements) both true divisions are done;
-//       * rows whose approximate maximum is below 2^-96, or whose smoothing
-//         values lie outside [2^-120, 2^120], where subnormal intermediates
-//         void the relative error bounds, take the exact path throughout;
+//       * where subnormal intermediates void the relative error bounds the
+//         exact divisions are used throughout: a thread holding a smoothing
+//         value outside [2^-120, 2^120] (for its elements; its wave divides
+//         every element for the maximum), a wave whose approximate maximum is
+//         below 2^-96 (for its maximum), and a row whose maximum is below
+//         2^-96 (for every element);
 //   - the row maximum is a wave64 shuffle reduction, then per-wave partial
 //     maxima through LDS (max is exact, so order does not matter);
 //   - rows longer than the register budget (K > 32768) take an exact
@@ -92,19 +96,6 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return m;
 }
 
-// Block-wide OR of a flag.
-template <int NW>
-__device__ __forceinline__ bool block_any(bool v, int* red) {
-    const bool w = __any(v);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = w ? 1 : 0;
-    __syncthreads();
-    int o = 0;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) o |= red[i];
-    return o != 0;
-}
-
 // Resolve the source row; an index outside [0, x_rows) marks the row invalid.
 __device__ __forceinline__ bool source_row(const int32_t* row_idx, int64_t m, int64_t x_rows,
                                            int64_t* src) {
@@ -134,17 +125,17 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
     const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
     float* __restrict__ sx, const float* __restrict__ amax_in) {
     constexpr int NW = T / 64;
-    __shared__ float redf[4][NW];
-    __shared__ int redi[NW];
+    __shared__ float redf[2][NW];
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
     const int K4 = static_cast<int>(K >> 2);
     const int t = threadIdx.x;
 
     // per-column reciprocals of the smoothing values, shared by the block's
     // rows (the smoothing values themselves are reloaded on the rare exact
-    // paths)
+    // paths).  A thread holding a smoothing value outside [2^-120, 2^120]
+    // takes the exact divisions for all of its elements.
     float4 rv[NV];
-    bool odd_s = false;
+    bool odd_t = false;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int j = t + i * T;
@@ -152,9 +143,8 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
         rv[i] = make_float4(fast_rcp(sv.x), fast_rcp(sv.y), fast_rcp(sv.z), fast_rcp(sv.w));
         const float lo = fminf(fminf(sv.x, sv.y), fminf(sv.z, sv.w));
         const float hi = fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w));
-        odd_s |= !(lo >= 0x1p-120f && hi <= 0x1p120f);
+        odd_t |= !(lo >= 0x1p-120f && hi <= 0x1p120f);
     }
-    const bool odd_cols = block_any<NW>(odd_s, redi);
 
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
     for (int rr = 0; rr < ROWS; ++rr) {
@@ -165,7 +155,7 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
         const float4* xr = reinterpret_cast<const float4*>(x + src * ldx);
 
         float4 xv[NV];
-        float amax_a = 0.0f;
+        float amax_loc = 0.0f;   // this thread's approximate maximum
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int j = t + i * T;
@@ -173,46 +163,50 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
             if constexpr (!GIVEN) {
                 const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y,
                                               xv[i].z * rv[i].z, xv[i].w * rv[i].w);
-                amax_a = absmax4(amax_a, ap);
+                amax_loc = absmax4(amax_loc, ap);
             }
         }
-        float* red0 = redf[(2 * rr) & 3];
-        float* red1 = redf[(2 * rr + 1) & 3];
         float amax = 0.0f;
-        bool exact_row;
         bool valid = ok;
         if constexpr (GIVEN) {
             // a given maximum: no reduction over the row.  A NaN or negative
             // one marks the row invalid, like a bad row index.
             amax = amax_in[m];
             valid = ok && amax >= 0.0f;
-            exact_row = odd_cols || !(amax >= 0x1p-96f);
         } else {
-        amax_a = block_max<NW>(amax_a, red0);
-        exact_row = odd_cols || !(amax_a >= 0x1p-96f);
-
-        // exact maximum: true divisions for the candidates only (or every
-        // element on an exact row)
-        const float thresh = amax_a * (1.0f - 0x1p-19f);
+            // This wave's exact maximum: the element holding it has an
+            // approximation within 2^-21 of the wave's approximate maximum
+            // (a shuffle reduction, no barrier), so only elements within
+            // 2^-19 of it -- usually one per wave -- are divided exactly; all
+            // of the wave's are when the approximations cannot be trusted
+            // (an odd smoothing value in the wave, or a maximum below 2^-96).
+            // One block-wide maximum of the exact values gives the row's.
+            const float amax_w = wave_max(amax_loc);
+            const bool all_exact = __any(odd_t) || !(amax_w >= 0x1p-96f);
+            const float thresh = amax_w * (1.0f - 0x1p-19f);
+            float amax_t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int j = t + i * T;
-            if (j >= K4) continue;
-            const float xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            const float rs[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
-            bool any = exact_row;
+            for (int i = 0; i < NV; ++i) {
+                const int j = t + i * T;
+                if (j >= K4) continue;
+                const float xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                const float rs[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+                bool any = all_exact;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
-            if (any) {
-                const float4 sv = s4[j];
-                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+                for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
+                if (any) {
+                    const float4 sv = s4[j];
+                    const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (exact_row || fabsf(xs[c] * rs[c]) >= thresh) amax = fmaxf(amax, fabsf(xs[c] / ss[c]));
+                    for (int c = 0; c < 4; ++c)
+                        if (all_exact || fabsf(xs[c] * rs[c]) >= thresh)
+                            amax_t = fmaxf(amax_t, fabsf(xs[c] / ss[c]));
+                }
             }
+            amax = block_max<NW>(amax_t, redf[rr & 1]);
         }
-        amax = block_max<NW>(amax, red1);
-        }
+        // tiny rows (or odd smoothing values) take the exact divisions
+        const bool exact = odd_t || !(amax >= 0x1p-96f);
         const float scale = valid ? amax / 127.0f : 0.0f;
         if (t == 0) sx[m] = valid ? scale : quiet_nan();
         const float inv = fast_rcp(scale);
@@ -224,7 +218,7 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
             if (j >= K4) continue;
             uint32_t packed = 0;
             if (scale != 0.0f) {
-                if (exact_row) {
+                if (exact) {
                     const float4 sv = s4[j];
                     packed = pack4(quantize_exact(xv[i].x, sv.x, scale), quantize_exact(xv[i].y, sv.y, scale),
                                    quantize_exact(xv[i].z, sv.z, scale), quantize_exact(xv[i].w, sv.w, scale));
