@@ -142,6 +142,79 @@ def cpu_baseline(gu, dn, head, cand, seconds):
                       f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
 
 
+def short_request_graph(torch, B, synth):
+    """A 256-token request (gate+up, down at split-K 4, answer head over a
+    50000-row lm_head) run eagerly and replayed from one captured HIP graph;
+    the answer-head tables stay in device memory, so one capture serves
+    every request of the bucket."""
+    gu, dn, head = synth.short_request("gate_up"), synth.short_request("down"), synth.lm_head(V=50000)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    M = 256
+    x1, s1, w1, sw1 = d(gu["x"]), d(gu["smooth"]), d(gu["w"]), d(gu["sw"])
+    x2, s2, w2, sw2, r2 = d(dn["x"]), d(dn["smooth"]), d(dn["w"]), d(dn["sw"]), d(dn["r"])
+    wh, swh, sh = d(head["w"]), d(head["sw"]), d(head["smooth"])
+    xq1, sx1, y1 = e((M, gu["K"]), torch.int8), e((M,), torch.float32), e((M, gu["N"]), torch.float32)
+    xq2, sx2, y2 = e((M, dn["K"]), torch.int8), e((M,), torch.float32), e((M, dn["N"]), torch.float32)
+    ws = B.splitk_workspace(M, dn["N"], dn["K"], 4)
+    rows = torch.tensor([M - 1], dtype=torch.int32, device="cuda")
+    cand = torch.tensor([[3, 17, 4000, 49999]], dtype=torch.int32, device="cuda")
+    xq3, sx3 = e((1, dn["N"]), torch.int8), e((1,), torch.float32)
+    logits, probs = e((1, 4), torch.float32), e((1, 4), torch.float64)
+
+    def head_only():
+        B.w8a8_answer_head(y2, rows, sh, wh, swh, cand, xq=xq3, sx=sx3, logits=logits, probs=probs)
+
+    def step():
+        B.w8a8_quantize_act(x1, s1, xq=xq1, sx=sx1)
+        B.w8a8_gemm(xq1, sx1, w1, sw1, y=y1)
+        B.w8a8_quantize_act(x2, s2, xq=xq2, sx=sx2)
+        B.w8a8_gemm_splitk(xq2, sx2, w2, sw2, 4, residual=r2, y=y2, workspace=ws)
+        head_only()
+
+    def timed(fn, n=50):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    def isolated(fn, n=50):
+        # host wall clock of one call issued on an idle GPU, synchronised
+        ts = []
+        for _ in range(n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return 1e6 * float(np.median(ts))
+
+    out = {}
+    for name, fn in (("step", step), ("answer_head", head_only)):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        eager = timed(fn)
+        replay = timed(g.replay)
+        out[name] = {"eager_us": round(eager, 1), "graph_us": round(replay, 1),
+                     "eager_isolated_us": round(isolated(fn), 1),
+                     "graph_isolated_us": round(isolated(g.replay), 1),
+                     "launches": 8 if name == "step" else 3}
+    return out
+
+
 def row_parallel_rank(torch, B, x2, s2, w2, sw2, r2):
     """One rank's kernels of the row-parallel down projection (8192 x 5120 x
     17408 split over `ranks`), each timed alone: the slice maximum, the
@@ -366,6 +439,7 @@ def main():
 
     mid_m = mid_m_shapes(torch, B, best_read)
     row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2)
+    graph = short_request_graph(torch, B, synth)
 
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
@@ -398,7 +472,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
         "kernels_us_pct": kernels_pct, "mfma_ceiling": ceiling, "mid_m": mid_m,
-        "row_parallel_rank": row_parallel,
+        "row_parallel_rank": row_parallel, "short_request_graph": graph,
     }
     print(json.dumps(line), flush=True)
 
