@@ -63,9 +63,10 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_row_absmax.argtypes = [p, i64, p, p, i64, i64, p]
     L.oracle_quantize_act_amax.argtypes = [p, i64, p, p, p, i64, i64, p, p]
     L.oracle_epilogue_acc.argtypes = [p, p, p, p, p, i64, i64]
+    L.oracle_requantize_q8_0.argtypes = [p, p, p, i64, i64, p, p]
     for f in ("oracle_quantize_act", "oracle_gemm", "oracle_gemm_sampled", "oracle_gemm_acc",
               "oracle_readout_candidates", "oracle_num_threads", "oracle_row_absmax",
-              "oracle_quantize_act_amax", "oracle_epilogue_acc"):
+              "oracle_quantize_act_amax", "oracle_epilogue_acc", "oracle_requantize_q8_0"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -173,6 +174,22 @@ def epilogue_acc(acc, sx, sw, residual=None):
     _check(lib().oracle_epilogue_acc(_ptr(acc), _ptr(sx), _ptr(sw), _ptr(r), _ptr(y), M, N),
            "epilogue_acc")
     return y
+
+
+def requantize_q8_0(q, d_bits, smooth):
+    """Q8_0 weights (int8 codes q [N,K], binary16 block scales d_bits [N,K/32]
+    as uint16 bit patterns) smoothed by ``smooth`` [K] and requantised per
+    output channel: returns ``(wq int8 [N,K], sw float32 [N])``."""
+    q = _c(q, np.int8)
+    d_bits = _c(d_bits, np.uint16)
+    smooth = _c(smooth, np.float32)
+    N, K = q.shape
+    assert d_bits.shape == (N, K // 32) and smooth.shape == (K,)
+    wq = np.empty((N, K), dtype=np.int8)
+    sw = np.empty((N,), dtype=np.float32)
+    _check(lib().oracle_requantize_q8_0(_ptr(q), _ptr(d_bits), _ptr(smooth), N, K, _ptr(wq), _ptr(sw)),
+           "requantize_q8_0")
+    return wq, sw
 
 
 def gemm(xq, sx, w, sw, residual=None, splitk=1):

@@ -285,6 +285,60 @@ int oracle_gemm_acc(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int
     return err;
 }
 
+/* Startup requantisation of Q8_0 weights with SmoothQuant (review page,
+ * section "Compute shared evidence once": the Q8_0 weights are requantised
+ * with SmoothQuant at startup).  Q8_0 keeps blocks of 32 int8 codes along a
+ * weight row with one binary16 scale each: w = d * q.  SmoothQuant moves the
+ * activations' per-channel scale into the weights, x' = x / s and
+ * w' = w * s, so x'.w'^T = x.w^T.  The pages give neither the calibration of
+ * s nor the order of the operations; the plainest reading, with s given:
+ *   w'[n,k] = fl(fl(d[n, k/32] * q[n,k]) * s[k])   (d*q is exact in binary32)
+ *   sw[n]   = fl(max_k |w'[n,k]| / 127)
+ *   wq[n,k] = clamp(rne(fl(w'[n,k] / sw[n])), -127, 127), 0 when sw[n] = 0
+ * i.e. the same symmetric round-half-even rule as the activations, per
+ * output channel.  d is given as binary16 bit patterns. */
+static float oracle_f16_to_f32(uint16_t h) {
+    const int sign = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
+    float v;
+    if (e == 0) v = ldexpf((float)f, -24);                    /* subnormal or zero */
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexpf((float)(f | 1024), e - 25);
+    return sign ? -v : v;
+}
+
+int oracle_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth, int64_t N,
+                           int64_t K, int8_t* wq, float* sw) {
+    if (!q || !d || !smooth || !wq || !sw || N < 0 || K <= 0 || (K % 32) != 0) return ORACLE_ERR_ARG;
+    const int64_t nb = K / 32;
+    int64_t n;
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float w = oracle_f16_to_f32(d[n * nb + k / 32]) * (float)q[n * K + k];
+            float ws = w * smooth[k];
+            float ab = fabsf(ws);
+            if (ab > amax) amax = ab;
+        }
+        float s = amax / 127.0f;
+        sw[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c = 0;
+            if (s != 0.0f) {
+                float w = oracle_f16_to_f32(d[n * nb + k / 32]) * (float)q[n * K + k];
+                float ws = w * smooth[k];
+                float t = ws / s;
+                float r = oracle_round_half_even(t);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+                c = (int8_t)(int)r;
+            }
+            wq[n * K + k] = c;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* The epilogue of given exact accumulators (the integer partials of the
  * ranks already added): y[m,n] = epilogue(acc[m,n]).  An accumulator outside
  * the int32 range is an error. */
