@@ -142,6 +142,32 @@ def cpu_baseline(gu, dn, head, cand, seconds):
                       f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
 
 
+def startup_requantize(torch, B, w1, s1, w2, s2):
+    """One-off startup requantisation of Q8_0 weights with SmoothQuant (the
+    layer weights stand in for Q8_0 codes, with random binary16 block
+    scales): time and GB/s for the gate+up and down weights."""
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    for name, q, s in (("gate_up", w1, s1), ("down", w2, s2)):
+        N, K = q.shape
+        d = (torch.rand((N, K // 32), device="cuda", generator=g) * 1e-2 + 1e-4).to(torch.float16)
+        w = torch.empty_like(q)
+        sw = torch.empty((N,), dtype=torch.float32, device="cuda")
+        fn = lambda: B.w8a8_requantize_q8_0(q, d, s, w=w, sw=sw)
+        for _ in range(2):
+            fn()
+        t = Timer(torch)
+        for _ in range(5):
+            t.run("r", fn)
+        torch.cuda.synchronize()
+        us = t.mean_us("r")
+        nbytes = 2 * N * K + 2 * N * (K // 32) + 4 * K + 4 * N
+        out[name] = {"shape": [N, K], "us": round(us, 1), "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del d, w, sw
+    return out
+
+
 def short_request_graph(torch, B, synth):
     """A 256-token request (gate+up, down at split-K 4, answer head over a
     50000-row lm_head) run eagerly and replayed from one captured HIP graph;
@@ -440,6 +466,7 @@ def main():
     mid_m = mid_m_shapes(torch, B, best_read)
     row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2)
     graph = short_request_graph(torch, B, synth)
+    requant = startup_requantize(torch, B, w1, s1, w2, s2)
 
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
@@ -473,6 +500,7 @@ def main():
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
         "kernels_us_pct": kernels_pct, "mfma_ceiling": ceiling, "mid_m": mid_m,
         "row_parallel_rank": row_parallel, "short_request_graph": graph,
+        "startup_requantize_q8_0": requant,
     }
     print(json.dumps(line), flush=True)
 

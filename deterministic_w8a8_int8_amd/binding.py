@@ -42,6 +42,7 @@ SIGNATURES = {
     "w8a8_gemm_splitk": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
     "w8a8_readout_candidates": (_I32, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P]),
     "w8a8_candidate_softmax": (_I32, [_P, _I64, _I64, _P, _P]),
+    "w8a8_requantize_q8_0": (_I32, [_P, _P, _P, _I64, _I64, _P, _P, _P]),
     "w8a8_row_absmax": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P, _P]),
     "w8a8_quantize_act_amax": (_I32, [_P, _I64, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P]),
     "w8a8_gemm_int32": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P]),
@@ -223,6 +224,29 @@ def w8a8_readout_candidates(xq, sx, w_vocab, sw_vocab, cand, logits=None, err_fl
                                         _ptr(cand), C, _ptr(logits), _ptr(err_flag), _stream(stream)),
            "w8a8_readout_candidates")
     return logits
+
+
+def w8a8_requantize_q8_0(q, d_bits, smooth, w=None, sw=None, stream=None):
+    """Q8_0 codes q [N, K] (int8) with binary16 block scales d_bits
+    [N, K/32] (int16/uint16 bit patterns, or float16) smoothed by ``smooth``
+    [K] and requantised per output channel; returns (w int8 [N, K], sw fp32 [N])."""
+    _want(q, torch.int8, "q")
+    _want(smooth, torch.float32, "smooth")
+    if d_bits.dtype == torch.float16:
+        d_bits = d_bits.view(torch.int16)
+    if d_bits.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("d_bits must hold binary16 bit patterns (int16/uint16/float16)")
+    for t, n in ((q, "q"), (d_bits, "d_bits")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    N, K = q.shape
+    if d_bits.shape != (N, K // 32):
+        raise ValueError("d_bits must be [N, K/32]")
+    w = torch.empty((N, K), dtype=torch.int8, device=q.device) if w is None else w
+    sw = torch.empty((N,), dtype=torch.float32, device=q.device) if sw is None else sw
+    _check(_lib.w8a8_requantize_q8_0(_ptr(q), _ptr(d_bits), _ptr(smooth), N, K, _ptr(w), _ptr(sw),
+                                     _stream(stream)), "w8a8_requantize_q8_0")
+    return w, sw
 
 
 def w8a8_row_absmax(x, smooth, row_idx=None, amax=None, accumulate=False, stream=None):

@@ -230,6 +230,20 @@ int w8a8_epilogue_int32(const int32_t* parts, int S, const float* sx, const floa
     return hip_status(w8a8::launch_reduce(a, S, parts, static_cast<hipStream_t>(stream)));
 }
 
+int w8a8_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth, int64_t N, int64_t K,
+                         int8_t* w, float* sw, void* stream) {
+    if (N < 0) return W8A8_ERR_INVALID_ARG;
+    if (const int kc = check_k(K)) return kc;
+    if (N > kMaxDim) return W8A8_ERR_SHAPE;
+    if (N == 0) return W8A8_OK;
+    if (!q || !d || !smooth || !w || !sw) return W8A8_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(d, 2) || !aligned(smooth, 16) || !aligned(w, 16) || !aligned(sw, 4))
+        return W8A8_ERR_ALIGN;
+    const size_t bytes = static_cast<size_t>(N) * static_cast<size_t>(K);
+    if (overlaps(q, bytes, w, bytes) && q != w) return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_requantize_q8_0(q, d, smooth, N, K, w, sw, static_cast<hipStream_t>(stream)));
+}
+
 int w8a8_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs, void* stream) {
     if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
     return hip_status(w8a8::launch_candidate_softmax(logits, M, C, probs, static_cast<hipStream_t>(stream)));

@@ -90,6 +90,12 @@ struct SkinnyArgs {
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 
+// Startup requantisation of Q8_0 weights with SmoothQuant (requant.hip):
+// wq [N,K] and sw [N] from codes q [N,K], binary16 block scales d [N,K/32]
+// and the smoothing vector [K]; K % 4 == 0 and K % 32 == 0.
+hipError_t launch_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth, int64_t N,
+                                  int64_t K, int8_t* wq, float* sw, hipStream_t stream);
+
 // Candidate softmax in binary64, one fixed operation sequence (softmax.hip):
 // probs[m, c] for c < C <= 64; rows with a non-finite logit give NaN.
 hipError_t launch_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs,

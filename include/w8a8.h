@@ -223,6 +223,29 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
                             void* stream);
 
 /*
+ * w8a8_requantize_q8_0 -- startup requantisation of Q8_0 weights with
+ * SmoothQuant (review page, section "Compute shared evidence once": the
+ * Q8_0 weights are requantised with SmoothQuant at startup).  Q8_0 keeps
+ * blocks of 32 int8 codes along a weight row, each block with one binary16
+ * scale: w = d * q.  With the smoothing vector that divides the
+ * activations (x' = x / s), per output channel n:
+ *     w'[n,k] = fl(fl(d[n, k/32] * q[n,k]) * smooth[k])
+ *     sw[n]   = fl(max_k |w'[n,k]| / 127)
+ *     w[n,k]  = clamp(rne(fl(w'[n,k] / sw[n])), -127, 127)   (0 if sw[n] = 0)
+ * The result feeds w8a8_gemm as (w, sw).  The smoothing vector comes from
+ * calibration (not done here).
+ *
+ * q       device int8 [N,K] Q8_0 codes, 16-byte aligned; K a multiple of 64.
+ * d       device uint16 [N,K/32]: the binary16 bit patterns of the block
+ *         scales (2-byte aligned).
+ * smooth  device fp32 [K], 16-byte aligned.
+ * w, sw   device int8 [N,K] (16-byte aligned; may be q itself, else must not
+ *         overlap it) and fp32 [N].
+ */
+int w8a8_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth, int64_t N, int64_t K,
+                         int8_t* w, float* sw, void* stream);
+
+/*
  * Tensor-parallel row-parallel layers.  The review page, section "Bitwise
  * consistency is not lossless quantization", combines the integer partial
  * sums of the ranks before scaling.  A rank holds a K-slice of the

@@ -109,6 +109,14 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 65, p, nul, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 0, p, 4, p, nul, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_readout_candidates(p, p, 3, 64, p, p, 10, p, 0, p, nul, S) == B.W8A8_OK
+    # Q8_0 requantisation
+    assert lib.w8a8_requantize_q8_0(p, p, p, 4, 96, p, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_requantize_q8_0(p, p, p, -1, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_requantize_q8_0(odd, p, p, 4, 64, p, p, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_requantize_q8_0(p, odd, p, 4, 64, p, p, S) == B.W8A8_ERR_ALIGN
+    assert lib.w8a8_requantize_q8_0(p, p, nul, 4, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_requantize_q8_0(p, p, p, 4, 64, ctypes.c_void_p(p.value + 64), p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_requantize_q8_0(p, p, p, 0, 64, p, p, S) == B.W8A8_OK
     # candidate softmax
     assert lib.w8a8_candidate_softmax(p, 3, 65, p, S) == B.W8A8_ERR_TOO_MANY_CANDIDATES
     assert lib.w8a8_candidate_softmax(p, -1, 4, p, S) == B.W8A8_ERR_INVALID_ARG
