@@ -34,6 +34,7 @@ SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [_I32]),
     "w8a8_abi_version": (_I32, []),
     "w8a8_set_tile_override": (_I32, [_I32]),
+    "w8a8_gemm_plan": (_I32, [_I64, _I64, _I64, _I32, _I32, _P]),
     "w8a8_probe_mfma_ceiling": (_I32, [_I32, _I64, _I64, _P, _P, _P]),
     "w8a8_probe_stream_read": (_I32, [_P, _I64, _P, _P]),
     "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
@@ -84,6 +85,14 @@ def abi_version() -> int:
 
 def set_tile_override(kind: int) -> None:
     _check(_lib.w8a8_set_tile_override(int(kind)), "w8a8_set_tile_override")
+
+
+def w8a8_gemm_plan(M, N, K, splitk=1, residual=False) -> list:
+    """The kernel choice for a shape (host only): eight ints, see the header."""
+    out = (ctypes.c_int32 * 8)()
+    _check(_lib.w8a8_gemm_plan(int(M), int(N), int(K), int(splitk), int(bool(residual)),
+                               ctypes.cast(out, ctypes.c_void_p)), "w8a8_gemm_plan")
+    return list(out)
 
 
 def w8a8_probe_mfma_ceiling(operand_kind, blocks, iters, sink, stream=None) -> int:

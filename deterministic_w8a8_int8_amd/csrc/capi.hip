@@ -73,6 +73,17 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
     return W8A8_OK;
 }
 
+// The panel kernel takes M in (SKINNY_MAX_M, kPanelMaxM] unless the override
+// forces a tiled configuration (0..5) or the panel kernel (6, any M it fits).
+constexpr int64_t kPanelMaxM = 512;
+
+bool pick_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, w8a8::PanelPlan* pp) {
+    const int ov = w8a8::tile_override_value();
+    if (ov >= 0 && ov != w8a8::PANEL_OVERRIDE) return false;
+    if (ov < 0 && (M <= w8a8::SKINNY_MAX_M || M > kPanelMaxM)) return false;
+    return w8a8::plan_panel(M, N, K, max_splitk, residual, pp);
+}
+
 int run_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
              const float* residual, float* y, int64_t M, int64_t N, int64_t K, int splitk,
              void* workspace, hipStream_t stream) {
@@ -80,8 +91,11 @@ int run_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw
         w8a8::SkinnyArgs s{xq, sx, w, sw, residual, y, M, N, K, N, nullptr, N, 0, nullptr};
         return hip_status(w8a8::launch_skinny(s, stream));
     }
-    const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
     const GemmArgs a{xq, sx, w, sw, residual, y, M, N, K, nullptr};
+    w8a8::PanelPlan pp;
+    if (pick_panel(M, N, K, splitk, residual != nullptr, &pp))
+        return hip_status(w8a8::launch_panel(a, pp, workspace, stream));
+    const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
     return hip_status(w8a8::launch_gemm_tiled(a, plan, workspace, stream));
 }
 
@@ -106,7 +120,7 @@ const char* w8a8_status_string(int status) {
 int w8a8_abi_version(void) { return 10000; }
 
 int w8a8_set_tile_override(int kind) {
-    if (kind < -1 || kind >= w8a8::TILE_KINDS) return W8A8_ERR_INVALID_ARG;
+    if (kind < -1 || kind > w8a8::PANEL_OVERRIDE) return W8A8_ERR_INVALID_ARG;
     w8a8::set_tile_override(kind);
     return W8A8_OK;
 }
@@ -134,6 +148,29 @@ int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t
     if (M == 0) return W8A8_OK;
     const w8a8::QuantArgs a{x, ldx, x_rows, row_idx, smooth, M, K, xq, sx, nullptr};
     return hip_status(w8a8::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, int32_t* out) {
+    if (!out || M <= 0 || N <= 0 || check_k(K) != W8A8_OK || splitk < 1 || splitk > W8A8_MAX_SPLITK ||
+        M > kMaxDim || N > kMaxDim)
+        return W8A8_ERR_INVALID_ARG;
+    for (int i = 0; i < 8; ++i) out[i] = 0;
+    if (splitk == 1 && M <= w8a8::SKINNY_MAX_M) {
+        out[0] = 0;
+        return W8A8_OK;
+    }
+    w8a8::PanelPlan pp;
+    if (pick_panel(M, N, K, splitk, residual != 0, &pp)) {
+        int mw = 0, nb = 0;
+        w8a8::panel_kind_shape(pp.kind, &mw, &nb);
+        const int32_t v[8] = {2, pp.kind, pp.R, pp.P, pp.S, pp.kb_per_split, mw, nb};
+        for (int i = 0; i < 8; ++i) out[i] = v[i];
+        return W8A8_OK;
+    }
+    const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
+    const int32_t v[8] = {1, static_cast<int32_t>(plan.kind), plan.bm, plan.bn, plan.splitk, 0, 0, 0};
+    for (int i = 0; i < 8; ++i) out[i] = v[i];
+    return W8A8_OK;
 }
 
 int w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
@@ -209,6 +246,9 @@ int w8a8_gemm_int32(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int
     if (!xq || !w || !acc) return W8A8_ERR_INVALID_ARG;
     if (!aligned(xq, 16) || !aligned(w, 16) || !aligned(acc, 16)) return W8A8_ERR_ALIGN;
     const GemmArgs a{xq, nullptr, w, nullptr, nullptr, nullptr, M, N, K, acc};
+    w8a8::PanelPlan pp;
+    if (pick_panel(M, N, K, 1, false, &pp))
+        return hip_status(w8a8::launch_panel(a, pp, nullptr, static_cast<hipStream_t>(stream)));
     const GemmPlan plan = w8a8::plan_gemm(M, N, K, 1);
     return hip_status(w8a8::launch_gemm_tiled(a, plan, nullptr, static_cast<hipStream_t>(stream)));
 }

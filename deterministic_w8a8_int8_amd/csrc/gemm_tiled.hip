@@ -758,6 +758,7 @@ int tile_override = -1;
 }  // namespace
 
 void set_tile_override(int kind) { tile_override = kind; }
+int tile_override_value() { return tile_override; }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
     (void)K;

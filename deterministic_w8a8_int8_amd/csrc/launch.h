@@ -58,12 +58,33 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk);
+// Override of the kernel choice: -1 automatic, 0..TILE_KINDS-1 one tiled
+// configuration, PANEL_OVERRIDE the column-panel kernel wherever it fits.
+constexpr int PANEL_OVERRIDE = TILE_KINDS;
 void set_tile_override(int kind);
+int tile_override_value();
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk);
 hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspace,
                              hipStream_t stream);
 // y = epilogue(P_0 + ... + P_{S-1}) for S int32 slices [S,M,N] (row-major).
 hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipStream_t stream);
+
+// Column-panel GEMM for mid-sized M (gemm_panel.hip): R row splits, P column
+// panels and S K splits (S > 1 writes int32 partials to the workspace, S
+// slices of [M,N], then launch_reduce).  plan_panel picks the configuration
+// from (M, N, K, max_splitk, residual) alone, with S <= max_splitk; it returns
+// false when the kernel cannot hold the rows.
+struct PanelPlan {
+    int kind;          // template configuration (rows and columns per wave)
+    int R, P, S;
+    int kb_per_split;  // 64-byte K-blocks per K split
+    double est_us;     // the model's time estimate
+};
+bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, PanelPlan* out);
+bool panel_plan_valid(int64_t M, int64_t N, int64_t K, const PanelPlan& p);
+// Rows-per-wave and columns-per-panel limits (in blocks of 16) of a panel kind.
+bool panel_kind_shape(int kind, int* mw, int* nb);
+hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, hipStream_t stream);
 
 // Skinny-M GEMM (M <= SKINNY_MAX_M): the weight is streamed from HBM once and
 // every wave keeps 16 weight rows against all M activation rows.  With

@@ -76,10 +76,27 @@ int w8a8_abi_version(void);
  * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
  * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
  * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
- * stages, 5: as 4 with the epilogue stored straight from the accumulators).  It never changes a result bit, only speed.  It also changes the
- * split-K workspace size, so query the size again after changing it.
+ * stages, 5: as 4 with the epilogue stored straight from the accumulators);
+ * 6 forces the column-panel kernel wherever it can hold the rows (by default
+ * it runs for 64 < M <= 512).  It never changes a result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */
 int w8a8_set_tile_override(int kind);
+
+/*
+ * Diagnostic (host, no GPU call): which kernel w8a8_gemm_splitk would run
+ * for this shape, split bound and residual flag (w8a8_gemm is splitk 1),
+ * under the current tile override.  out: host int32[8], filled as
+ *   out[0] = 0: skinny kernel (M <= 64); rest 0.
+ *   out[0] = 1: tiled kernel; out[1] tile configuration, out[2] and out[3]
+ *            the tile's rows and columns, out[4] the K splits.
+ *   out[0] = 2: column-panel kernel; out[1] its configuration, out[2] row
+ *            splits R, out[3] column panels P, out[4] K splits S (at most
+ *            splitk), out[5] 64-byte K-blocks per split, out[6] row blocks
+ *            of 16 per wave (limit), out[7] column blocks of 16 per panel
+ *            (limit).
+ * Returns W8A8_ERR_INVALID_ARG for an invalid shape or a NULL out.
+ */
+int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, int32_t* out);
 
 /*
  * Diagnostic (not part of the layer): launch an MFMA-only kernel that runs

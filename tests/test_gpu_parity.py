@@ -156,7 +156,7 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5, 6])
 def test_every_tile_shape_gives_identical_bits(kind):
     M, N, K = 300, 520, 704
     say(f"tile kind {kind}")
@@ -184,6 +184,39 @@ def test_splitk_matches_oracle(M, N, K, splitk):
     for rep in range(2):  # and it serves the next call as it is left
         got = host(B.w8a8_gemm_splitk(xq_d, sx_d, w_d, sw_d, splitk, residual=r_d, workspace=ws))
         assert_bits_equal(got, want, f"split {splitk} rep {rep}")
+
+
+# Column-panel kernel (64 < M <= 512 by default; forced here on ragged shapes):
+# N not a multiple of 4 (scalar epilogue), K not a multiple of 256 (short
+# last LDS stage), fewer row blocks than waves, panels of unequal width.
+PANEL_SHAPES = [(65, 100, 64), (80, 17, 128), (96, 1001, 448), (130, 300, 1024), (200, 257, 192),
+                (257, 513, 1216), (300, 2100, 704), (333, 555, 1088), (512, 260, 320),
+                (17, 333, 256), (1, 50, 320)]
+
+
+@pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
+def test_panel_kernel_matches_oracle(M, N, K):
+    say(f"panel M={M} N={N} K={K}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=2 * M + 3 * N + K, residual=True)
+    want_r = oracle.gemm(xq, sx, w, sw, r)
+    want = oracle.gemm(xq, sx, w, sw)
+    d = [dev(xq), dev(sx), dev(w), dev(sw)]
+    B.set_tile_override(6)
+    try:
+        got = host(B.w8a8_gemm(*d))
+        got_r = host(B.w8a8_gemm(*d, residual=dev(r)))
+        got_s3 = host(B.w8a8_gemm_splitk(*d, 3, residual=dev(r)))
+        got_s5 = host(B.w8a8_gemm_splitk(*d, 5))
+        acc = host(B.w8a8_gemm_int32(d[0], d[2]))
+        plans = [B.w8a8_gemm_plan(M, N, K, s, res) for s, res in ((1, 0), (3, 1), (5, 0))]
+    finally:
+        B.set_tile_override(-1)
+    say(f"  plans {plans}")
+    assert_bits_equal(got, want, "panel")
+    assert_bits_equal(got_r, want_r, "panel + residual")
+    assert_bits_equal(got_s3, want_r, "panel split<=3 + residual")
+    assert_bits_equal(got_s5, want, "panel split<=5")
+    np.testing.assert_array_equal(acc, oracle.gemm_acc(xq, w))
 
 
 def test_splitk_more_chunks_than_kblocks():
