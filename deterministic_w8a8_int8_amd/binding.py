@@ -88,8 +88,8 @@ def set_tile_override(kind: int) -> None:
 
 
 def w8a8_gemm_plan(M, N, K, splitk=1, residual=False) -> list:
-    """The kernel choice for a shape (host only): eight ints, see the header."""
-    out = (ctypes.c_int32 * 8)()
+    """The kernel choice for a shape (host only): ten ints, see the header."""
+    out = (ctypes.c_int32 * 10)()
     _check(_lib.w8a8_gemm_plan(int(M), int(N), int(K), int(splitk), int(bool(residual)),
                                ctypes.cast(out, ctypes.c_void_p)), "w8a8_gemm_plan")
     return list(out)

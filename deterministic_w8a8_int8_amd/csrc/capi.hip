@@ -154,22 +154,22 @@ int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, in
     if (!out || M <= 0 || N <= 0 || check_k(K) != W8A8_OK || splitk < 1 || splitk > W8A8_MAX_SPLITK ||
         M > kMaxDim || N > kMaxDim)
         return W8A8_ERR_INVALID_ARG;
-    for (int i = 0; i < 8; ++i) out[i] = 0;
+    for (int i = 0; i < 10; ++i) out[i] = 0;
     if (splitk == 1 && M <= w8a8::SKINNY_MAX_M) {
         out[0] = 0;
         return W8A8_OK;
     }
     w8a8::PanelPlan pp;
     if (pick_panel(M, N, K, splitk, residual != 0, &pp)) {
-        int mw = 0, nb = 0;
-        w8a8::panel_kind_shape(pp.kind, &mw, &nb);
-        const int32_t v[8] = {2, pp.kind, pp.R, pp.P, pp.S, pp.kb_per_split, mw, nb};
-        for (int i = 0; i < 8; ++i) out[i] = v[i];
+        int mw = 0, nb = 0, nset = 0, nslot = 0;
+        w8a8::panel_kind_shape(pp.kind, &mw, &nb, &nset, &nslot);
+        const int32_t v[10] = {2, pp.kind, pp.R, pp.P, pp.S, pp.kb_per_split, mw, nb, nset, nslot};
+        for (int i = 0; i < 10; ++i) out[i] = v[i];
         return W8A8_OK;
     }
     const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
-    const int32_t v[8] = {1, static_cast<int32_t>(plan.kind), plan.bm, plan.bn, plan.splitk, 0, 0, 0};
-    for (int i = 0; i < 8; ++i) out[i] = v[i];
+    const int32_t v[10] = {1, static_cast<int32_t>(plan.kind), plan.bm, plan.bn, plan.splitk, 0, 0, 0, 0, 0};
+    for (int i = 0; i < 10; ++i) out[i] = v[i];
     return W8A8_OK;
 }
 

@@ -19,14 +19,16 @@
 //   - the 4 waves split the rows (mw <= MW blocks of 16 rows each) and all
 //     of them sweep the whole panel, so every weight byte is fetched from
 //     HBM once per workgroup and each activation row once per panel;
-//   - the weight panel goes HBM -> VGPR -> LDS through a ring of 3 stages of
-//     4 K-blocks (256 bytes of K per row).  A stage is loaded one stage
-//     ahead and written to LDS at the end of the next stage, into the ring
-//     slot freed by the barrier at its start.  16-byte chunks of a row are
-//     XOR-swizzled with the row index, so the 16 rows one fragment read
-//     touches hit distinct banks;
-//   - activation fragments go HBM/L2 -> VGPR directly (each wave reads only
-//     its own rows), two K-blocks ahead of their use;
+//   - a stage is two 64-byte K-blocks of every row the workgroup touches:
+//     its activation rows, then its weight rows.  Stages go HBM/L2 -> VGPR
+//     -> LDS with loads that read 8 rows x 128 bytes per wave instruction
+//     (whole cache lines: an instruction in MFMA fragment layout, 16 rows x
+//     64 bytes, sustains about a third of the L2 bandwidth on MI355X), then
+//     both operands' fragments are read from LDS.  NSET register sets keep
+//     NSET stages in flight; NSLOT LDS slots (3 when they fit) let the next
+//     stage's first fragments be read before the barrier;
+//   - 16-byte chunks of a row are XOR-swizzled with the row index, so the 16
+//     rows one fragment read touches hit distinct banks;
 //   - v_mfma_i32_16x16x64_i8 with the weight fragment as first operand: lane
 //     l, element e of a 16x16 tile is output row (l % 16) and column
 //     4*(l/16) + e, so each lane stores four adjacent outputs of one row with
@@ -37,7 +39,9 @@
 //     its own slice of the workspace, and the split-K reduction kernel adds
 //     the slices in order and runs the epilogue.
 // All memory operations are ordinary loads and stores, so the compiler's
-// own wait counts order them; nothing waits on a copy it does not need.
+// own wait counts order them.  Only staging loads use the vector-memory
+// counter in the main loop; it retires them in issue order, which is the
+// order they are needed in.
 #include <algorithm>
 #include <type_traits>
 
@@ -50,9 +54,8 @@ namespace {
 
 constexpr int NXCD = 8;             // XCDs on MI355X
 constexpr int PANEL_THREADS = 256;  // 4 waves, one per SIMD
-constexpr int KBS = 4;              // 64-byte K-blocks per LDS stage
-constexpr int NSTB = 3;             // LDS ring stages
-constexpr int ROW_BYTES = 64 * KBS; // bytes of one weight row in a stage
+constexpr int KBS = 2;              // 64-byte K-blocks per stage
+constexpr int ROW_BYTES = 64 * KBS; // bytes of one row in a stage (8 chunks of 16)
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
 
 struct PanelParams {
@@ -62,13 +65,32 @@ struct PanelParams {
     int S, kb_per_split;        // K splits (64-byte K-blocks per split)
 };
 
-template <int MW, int NB, bool DEEP>
+// Chunk swizzle of an LDS row: the 16 rows that one fragment read touches
+// (same logical chunk) land in 16 distinct 16-byte bank groups of 256 bytes
+// (64 banks), and any 8 consecutive rows in 8 distinct groups of 128 bytes.
+__device__ __forceinline__ int panel_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Smallest divisor of g that is at least `want` (the fragment ring's size:
+// its phase must repeat every stage).
+constexpr int ring_size(int g, int want) {
+    for (int d = want; d <= g; ++d)
+        if (g % d == 0) return d;
+    return g;
+}
+
+template <int MW, int NB, int NSET, int NSLOT>
 __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, const float* residual, float* y, int32_t* __restrict__ partials,
     PanelParams pp) {
-    constexpr int STAGE_BYTES = NB * 16 * ROW_BYTES;
-    __shared__ __attribute__((aligned(1024))) int8_t smem[NSTB * STAGE_BYTES];
+    constexpr int AR = 64 * MW;                      // activation rows of a stage (4 waves)
+    constexpr int BR = 16 * NB;                      // weight rows of a stage
+    constexpr int RPAD = (AR + BR + 31) / 32 * 32;   // rows incl. padding: whole load instructions
+    constexpr int QPT = RPAD / 32;                   // 16-byte pieces per thread per stage
+    constexpr int QA = AR / 32;                      // of which activation pieces
+    constexpr int STAGE_BYTES = RPAD * ROW_BYTES;
+    static_assert(NSLOT == 2 || NSLOT == 3, "LDS slots");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NSLOT * STAGE_BYTES];
 
     const int M = pp.M, N = pp.N, K = pp.K;
     // ---- block -> (panel, K split, row split); consecutive ids share an XCD,
@@ -95,80 +117,76 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
     // rows: split r gets row blocks [rs0, rs1); wave w a balanced share of them
     const int rs0 = r * pp.rb_total / pp.R, rs1 = (r + 1) * pp.rb_total / pp.R;
     const int nrb = rs1 - rs0;
-    const int rbw = rs0 + wave * nrb / 4;
-    const int mw = rs0 + (wave + 1) * nrb / 4 - rbw;   // <= MW (host-checked)
+    // (wave w owns row blocks [rs0 + w*nrb/4, rs0 + (w+1)*nrb/4), at most MW:
+    // host-checked)
+    const int row_end = min(16 * rs1, M);             // rows of this split: [16 rs0, row_end)
+    const int row_first = min(16 * rs0, M - 1);
 
-    // ---- weight staging: thread t copies chunk (t % 16) of row t/16 + 16q of
-    // the stage, for q < NB.  Stored at physical chunk t % 16 of that row,
-    // which holds logical chunk (t % 16) ^ (t / 16).  Column blocks past the
-    // panel (q >= ncb) re-read block ncb-1 (a cache hit, no extra HBM
-    // traffic) into LDS rows nobody stores results from, so every thread
-    // issues the same loads in every stage: the compiler's wait counts then
-    // need no merge over paths.  DEEP: two staging sets keep two stages (2 x
-    // NB x 4 KiB per CU) of weights in flight (the stream is latency-bound:
-    // bandwidth = bytes in flight / latency); otherwise one.
+    // ---- staging.  Thread t's piece q is 16-byte chunk t % 8 (physical) of
+    // stage row (t / 8) + 32 q, which holds logical chunk (t % 8) ^ swz(row)
+    // (the swizzle depends on t alone).  Pieces q < QA are activation rows:
+    // stage row w*16*MW + x is row 16*rbw(w) + x of the matrix; the others
+    // are weight rows of the panel.  Every read is a raw buffer
+    // load over exactly this panel's weight rows or this split's activation
+    // rows: a fixed 32-bit per-lane offset plus a scalar stage offset, no
+    // address arithmetic in the loop.
     const int t = threadIdx.x;
-    const int st_lc = (t & 15) ^ (t >> 4);
-    // All global reads are raw buffer loads: a 32-bit per-lane offset fixed
-    // for the whole loop, plus a scalar offset for the stage or K-block, so
-    // no address arithmetic sits in the loop.  The buffer ranges cover
-    // exactly this panel's weight rows and this row split's activation rows;
-    // the hardware returns zeros past them (every read here is inside by
-    // construction).
-    const int b_rows = min(c0 + NB * 16, N) - c0;
+    const int st_pc = t & 7;
+    const int st_lc = st_pc ^ panel_swz(t >> 3);
+    const int b_rows = min(c0 + BR, N) - c0;
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(B + static_cast<int64_t>(c0) * K), 0, b_rows * K, kBufferFlags);
-    uint32_t b_off[NB];   // byte offset of the row (clamped to N-1) and chunk inside the panel
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(A + static_cast<int64_t>(row_first) * K), 0, (row_end - row_first) * K, kBufferFlags);
+    // Rows no result is stored from (a wave's row blocks past its mw, column
+    // blocks past the panel, padding) get an offset past the buffer's range:
+    // the hardware returns zeros without touching memory, so they cost no
+    // bandwidth and the matrix cores multiply zeros (less power).
+    constexpr int kOutOfRange = 0x40000000;   // beyond every buffer range here (< 2^31 with offsets)
+    int q_off[QPT];
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-        const int col = min(c0 + 16 * min(q, ncb - 1) + (t >> 4), N - 1);
-        b_off[q] = static_cast<uint32_t>(col - c0) * static_cast<uint32_t>(K) + st_lc * 16;
+    for (int q = 0; q < QPT; ++q) {
+        const int sr = (t >> 3) + 32 * q;   // stage row
+        if (q < QA) {
+            const int w = sr / (16 * MW), x = sr % (16 * MW);
+            const int rbw_w = rs0 + w * nrb / 4;
+            const int mw_w = rs0 + (w + 1) * nrb / 4 - rbw_w;
+            const int row = min(16 * rbw_w + x, row_end - 1);
+            const bool own = x < 16 * mw_w && 16 * rbw_w + x < row_end;
+            q_off[q] = own ? (row - row_first) * K + st_lc * 16 : kOutOfRange;
+        } else {
+            const int br = sr - AR;
+            const int col = min(c0 + br, N - 1);
+            q_off[q] = (br < 16 * ncb && c0 + br < N) ? (col - c0) * K + st_lc * 16 : kOutOfRange;
+        }
     }
-    constexpr int NSET = DEEP ? 2 : 1;   // weight staging register sets
-    constexpr int NPAIR = DEEP ? 4 : 2;  // activation pair buffers
-    i32x4 bs[NSET][NB];
-    // Load stage st (clamped to the last stage) into `dst`.  In a short last
-    // stage the chunks past its K-blocks re-read chunk lc % 4 (inside the
-    // stage's first K-block, so inside the matrix); those bytes are never
-    // multiplied.
-    auto stage_load = [&](i32x4* dst, int st) __attribute__((always_inline)) {
+    // Piece q of stage st (clamped to the last stage).  In a short last stage
+    // the chunks of its missing K-block re-read the stage's first K-block
+    // (inside the matrix); those bytes are never multiplied.
+    auto piece_load = [&](i32x4& dst, int st, int q) __attribute__((always_inline)) {
         st = min(st, nst - 1);
-        const int kin = nkb - st * KBS;
-        const int lcd = ((st_lc >> 2) < kin ? 0 : (st_lc & 3) - st_lc) * 16;
-        const int soff = (kb0 * 64) + st * ROW_BYTES;
+        const int lcd = ((st_lc >> 2) < nkb - st * KBS) ? 0 : -64;
+        dst = __builtin_amdgcn_raw_buffer_load_b128(q < QA ? ra : rb, q_off[q] + lcd, (kb0 + st * KBS) * 64, 0);
+    };
+    auto piece_store = [&](const i32x4& src, int slot_, int q) __attribute__((always_inline)) {
+        *reinterpret_cast<i32x4*>(smem + slot_ * STAGE_BYTES + 16 * t + q * 32 * ROW_BYTES) = src;
+    };
+    auto stage_load = [&](i32x4* dst, int st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < NB; ++q)
-            dst[q] = __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<int>(b_off[q]) + lcd, soff, 0);
+        for (int q = 0; q < QPT; ++q) piece_load(dst[q], st, q);
     };
     auto stage_store = [&](const i32x4* src, int slot_) __attribute__((always_inline)) {
-        int8_t* dst = smem + slot_ * STAGE_BYTES + 16 * t;
 #pragma unroll
-        for (int q = 0; q < NB; ++q) *reinterpret_cast<i32x4*>(dst + q * 16 * ROW_BYTES) = src[q];
+        for (int q = 0; q < QPT; ++q) piece_store(src[q], slot_, q);
     };
 
-    // ---- fragment addresses.  Weight fragment (column block j, K-block u of
-    // a stage): row 16j + l%16, logical chunk 4u + l/16, physical chunk
-    // (4u + l/16) ^ (l%16).
+    // ---- fragment addresses: row x of a 16-row block, K-block u of the stage:
+    // logical chunk 4u + l/16, physical chunk (4u + l/16) ^ swz(l % 16).
     const int f_row = lane & 15;
-    const int f_grp = lane >> 4;
     int f_off[KBS];
 #pragma unroll
-    for (int u = 0; u < KBS; ++u) f_off[u] = f_row * ROW_BYTES + (((4 * u + f_grp) ^ f_row) * 16);
-    // Activation fragment (row block i of the wave, K-block kb): row
-    // 16*(rbw+i) + l%16 (clamped to M-1), bytes 64*kb + 16*(l/16).
-    const int a_row0 = 16 * rs0;
-    const int a_rows = max(min(16 * rs1, M) - a_row0, 1);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t*>(A + static_cast<int64_t>(min(a_row0, M - 1)) * K), 0, a_rows * K, kBufferFlags);
-    int a_off[MW];
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-        const int row = min(16 * (rbw + i) + f_row, min(16 * rs1, M) - 1);
-        a_off[i] = (row - min(a_row0, M - 1)) * K + 16 * f_grp;
-    }
-    auto a_frag = [&](int i, int kbc) __attribute__((always_inline)) -> i32x4 {   // kbc: clamped K-block
-        return __builtin_amdgcn_raw_buffer_load_b128(ra, a_off[i], (kb0 + kbc) * 64, 0);
-    };
+    for (int u = 0; u < KBS; ++u) f_off[u] = f_row * ROW_BYTES + (((4 * u + (lane >> 4)) ^ panel_swz(f_row)) * 16);
+    const int a_base = wave * 16 * MW * ROW_BYTES;   // this wave's activation rows in a stage
 
     i32x4 acc[MW][NB];
 #pragma unroll
@@ -176,168 +194,171 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-    // Activation fragments of two consecutive K-blocks (a "pair").  Every wave
-    // runs all MW x NB products: rows past its own (i >= mw) multiply clamped
-    // rows and columns past the panel (j >= ncb) multiply stale LDS rows;
-    // neither is ever stored, and in lockstep waves and panels the busiest one
-    // sets the time anyway.  K-block indices past the split are clamped to its
-    // last K-block (in-bounds reads whose products are never added).
-    struct APair {
-        i32x4 v[MW][2];
-    };
-    auto load_a = [&](APair& ap, int kb) __attribute__((always_inline)) {   // K-blocks kb, kb+1 of this split
-        const int k0 = min(kb, nkb - 1), k1 = min(kb + 1, nkb - 1);
-#pragma unroll
-        for (int i = 0; i < MW; ++i) {
-            ap.v[i][0] = a_frag(i, k0);
-            ap.v[i][1] = a_frag(i, k1);
-        }
-    };
-
-    // Weight fragments go through a ring of RING registers.  A stage is
-    // G = 4*NB groups (group g: K-block g / NB, column block g % NB); group g
-    // runs MW MFMAs on ring register g % RING, and right after its first MFMA
-    // the wave reads the fragment of group g + RING - 1 (past the stage's end:
-    // the next stage's first groups, whose slot is already published).
-    constexpr int RING = MW >= 3 ? 4 : 8;
+    // Every wave runs all MW x NB products: rows past its own (i >= mw) and
+    // columns past the panel (j >= ncb) are zeros in LDS and are never
+    // stored; in lockstep waves and panels the busiest one sets the time
+    // anyway.
+    //
+    // Fragments: the activation fragments of a K-block (af[u]) are read
+    // during the previous K-block; weight fragments go through a ring of RING
+    // registers: a stage is G = KBS*NB groups (group g: K-block g / NB, column
+    // block g % NB), group g runs MW MFMAs on ring register g % RING, and
+    // right after its first MFMA the wave reads the fragment of group
+    // g + RING - 1.
     constexpr int G = KBS * NB;
+    constexpr int RING = ring_size(G, MW >= 3 ? 4 : 8);
     static_assert(G % RING == 0, "the ring phase must repeat every stage");
     i32x4 fr[RING];
-    auto read_frag = [&](int slot_, int g) __attribute__((always_inline)) {
+    i32x4 af[KBS][MW];
+    auto read_b = [&](int slot_, int g) __attribute__((always_inline)) {
         fr[g % RING] = *reinterpret_cast<const i32x4*>(smem + slot_ * STAGE_BYTES + f_off[g / NB] +
-                                                       (g % NB) * 16 * ROW_BYTES);
+                                                       (AR + 16 * (g % NB)) * ROW_BYTES);
+    };
+    auto read_a = [&](int slot_, int u, int i) __attribute__((always_inline)) {
+        af[u][i] = *reinterpret_cast<const i32x4*>(smem + slot_ * STAGE_BYTES + a_base + f_off[u] +
+                                                   16 * i * ROW_BYTES);
     };
 
+    i32x4 bs[NSET][QPT];
+    constexpr bool PRE = NSLOT == 3;   // next stage readable before the barrier
+
     // ---- one stage; the instruction order is written out and pinned with
-    // scheduling barriers (the compiler would otherwise sink every prefetch to
+    // scheduling barriers (the compiler would otherwise sink every read to
     // its first use), and the compiler places the waits.
-    //   - Stage st uses ring slot st % 3.  Activation pair p (K-blocks 2p,
-    //     2p+1 of the split) lives in buffer p % NPAIR: stage st multiplies
-    //     pairs 2st and 2st+1.  During K-block 0 the wave loads pair
-    //     2st + NPAIR - 1 and during K-block 2 pair 2st + NPAIR, each into the
-    //     buffer the previous pair just released: activations run 2*NPAIR - 2
-    //     K-blocks ahead.
-    //   - During K-block 2, after that prefetch, staging set st % NSET (stage
-    //     st+2, loaded NSET stages ago) goes to the slot stage st-1 used (free
-    //     since the barrier at the top of this stage; the next barrier
-    //     publishes it before anyone reads it), and stage st + 2 + NSET starts
-    //     loading into it.
-    //   - The vector-memory counter retires loads in issue order, so a wait
-    //     for an activation pair also waits for every weight load issued
-    //     before it.  The first pair loaded after a weight load is used
-    //     2*NPAIR - 2 K-blocks later, at K-block 2 NSET stages on (NPAIR =
-    //     2*NSET), exactly when that weight load is stored: the weights keep
-    //     their NSET stages of lead.
-    // FULL: all 4 K-blocks present (every stage but a short last one); ODD:
-    // the parity of st, which fixes the buffers at compile time.
-    APair abuf[NPAIR];
-    auto run_stage = [&](int st, auto full_tag, auto odd_tag) __attribute__((always_inline)) {
+    //   - Stage st uses LDS slot st % NSLOT.  With 3 slots stage X is written
+    //     during stage X-2 (into the slot stage X-3 used, free since the
+    //     barrier at the top of stage X-2) and published by the barrier at the
+    //     top of stage X-1, so the last K-block of a stage reads the first
+    //     fragments of the next.  With 2 slots it is written during stage X-1
+    //     and published at the top of stage X.
+    //   - Staging set SET holds the stage to write (loaded NSET stages ago);
+    //     piece by piece it goes to LDS and the piece of the stage NSET
+    //     further on is loaded into its register.  Staging loads are the only
+    //     vector-memory reads in the loop, and they are needed in issue order.
+    //   - With one wave per SIMD, a memory instruction that has to wait for
+    //     its queue stalls the matrix pipe, so after every MFMA the wave
+    //     issues at most one weight-fragment read (right after the first MFMA
+    //     of a column block) and one other memory instruction: the next
+    //     K-block's activation fragments first, then this K-block's half of
+    //     the staging stores and loads.
+    // FULL: both K-blocks present (every stage but a short last one).
+    auto run_stage = [&](int st, auto full_tag, auto set_tag) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_tag)::value;
-        constexpr int ODD = decltype(odd_tag)::value;
-        constexpr int SET = NSET == 2 ? ODD : 0;
-        if (st > 0) __syncthreads();
-        const int slot_ = st % NSTB;
-        const int nslot = (st + 1) % NSTB;
-        const int kin = FULL ? KBS : nkb - st * KBS;   // K-blocks in this stage (uniform)
-        const int kb = st * KBS;
+        constexpr int SET = decltype(set_tag)::value;
+        if (st > 0) {
+            __syncthreads();
+            if constexpr (!PRE) {
+                const int sl = st % NSLOT;
+#pragma unroll
+                for (int i = 0; i < MW; ++i) read_a(sl, 0, i);
+#pragma unroll
+                for (int g = 0; g < RING - 1; ++g) read_b(sl, g);
+            }
+        }
+        const int slot_ = st % NSLOT;
+        const int nslot = (st + 1) % NSLOT;
+        const int kin = FULL ? KBS : nkb - st * KBS;
+        const int wslot = (st + NSLOT - 1) % NSLOT;   // slot of the stage being written
+        const int lst = st + NSLOT - 1 + NSET;        // stage being loaded
+        constexpr int QH = (QPT + 1) / 2;             // staging pieces handled in K-block 0
 #pragma unroll
         for (int u = 0; u < KBS; ++u) {
             if (!FULL && u >= kin) break;                // (uniform)
-            const APair& cur = abuf[(2 * ODD + (u >> 1)) % NPAIR];
-            const int h = u & 1;
-            // prefetch during K-blocks 0 and 2: pair 2st + u/2 + NPAIR - 1
-            APair* al = (u & 1) ? nullptr : &abuf[(2 * ODD + (u >> 1) + NPAIR - 1) % NPAIR];
-            const int ak0 = min(kb + u + 2 * NPAIR - 2, nkb - 1), ak1 = min(kb + u + 2 * NPAIR - 1, nkb - 1);
-            int issued = 0;
+            // next K-block's activation fragments: the other K-block of this
+            // stage, or (with PRE) K-block 0 of the next stage
+            const bool a_next = u + 1 < KBS || PRE;
+            const int a_slot = u + 1 < KBS ? slot_ : nslot;
+            const int a_u = (u + 1) % KBS;
+            const int na = a_next ? MW : 0;
+            const int q0 = u == 0 ? 0 : QH, q1 = u == 0 ? QH : QPT;
+            const int nsec = na + (FULL ? 2 * (q1 - q0) : 0);   // secondary memory instructions
+            int sec = 0;
+            auto secondary = [&]() __attribute__((always_inline)) {
+                if (sec < na) {
+                    read_a(a_slot, a_u, sec);
+                } else {
+                    const int k = sec - na, q = q0 + (k >> 1);
+                    if ((k & 1) == 0) piece_store(bs[SET][q], wslot, q);
+                    else piece_load(bs[SET][q], lst, q);
+                }
+                ++sec;
+                __builtin_amdgcn_sched_barrier(0);
+            };
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int g = u * NB + j;
 #pragma unroll
                 for (int i = 0; i < MW; ++i) {
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fr[g % RING], cur.v[i][h], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fr[g % RING], af[u][i], acc[i][j], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     if (i == 0) {
                         const int gn = g + RING - 1;
-                        read_frag(gn < G ? slot_ : nslot, gn < G ? gn : gn - G);
-                        __builtin_amdgcn_sched_barrier(0);
-                    } else if (al && issued < 2 * MW) {
-                        const int li = issued >> 1, lh = issued & 1;
-                        al->v[li][lh] = a_frag(li, lh ? ak1 : ak0);
-                        ++issued;
-                        __builtin_amdgcn_sched_barrier(0);
+                        if (gn < G || PRE) {
+                            read_b(gn < G ? slot_ : nslot, gn < G ? gn : gn - G);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
+                    if ((i != 0 || MW == 1) && sec < nsec) secondary();
                 }
             }
-            if (al) {
 #pragma unroll
-                for (int q = 0; q < 2 * MW; ++q)
-                    if (q >= issued) al->v[q >> 1][q & 1] = a_frag(q >> 1, (q & 1) ? ak1 : ak0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (FULL && u == 2) {
-                stage_store(bs[SET], (st + 2) % NSTB);
-                stage_load(bs[SET], st + 2 + NSET);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (!FULL) {   // a short last stage: nothing later reads these
-            stage_store(bs[SET], (st + 2) % NSTB);
-            stage_load(bs[SET], st + 2 + NSET);
+            for (int k = 0; k < na + 2 * QPT; ++k)
+                if (sec < nsec) secondary();
         }
     };
 
-    // ---- prologue: stages 0 and 1 into the ring with one memory latency
-    // (without DEEP, stage 1 borrows the fragment ring and a pair buffer as
-    // staging space), the next NSET stages in flight, activation pairs
-    // 0 .. NPAIR-2 and the first fragments in registers
+    // ---- prologue: the first NSLOT-1 stages into LDS (one memory latency),
+    // the next NSET in flight, the first fragments in registers
     if (nst > 0) {   // (uniform) an empty K split multiplies nothing
-        if constexpr (DEEP) {
-            stage_load(bs[0], 0);
-            stage_load(bs[1], 1);
+        static_assert(NSET >= NSLOT - 1, "prologue staging space");
 #pragma unroll
-            for (int pr = 0; pr + 1 < NPAIR; ++pr) load_a(abuf[pr], 2 * pr);
-            stage_store(bs[0], 0);
-            stage_store(bs[1], 1);
-            stage_load(bs[0], 2);
-            stage_load(bs[1], 3);
-        } else {
-            static_assert(RING + 2 * MW >= NB, "prologue staging space");
-            i32x4 tmp[RING + 2 * MW];
-            stage_load(bs[0], 0);
-            stage_load(tmp, 1);
-            load_a(abuf[0], 0);
-            stage_store(bs[0], 0);
-            stage_store(tmp, 1);
-            stage_load(bs[0], 2);
-        }
+        for (int x = 0; x < NSLOT - 1; ++x) stage_load(bs[x], x);
+#pragma unroll
+        for (int x = 0; x < NSLOT - 1; ++x) stage_store(bs[x], x);
+#pragma unroll
+        for (int x = 0; x < NSET; ++x) stage_load(bs[x], NSLOT - 1 + x);
         __syncthreads();
 #pragma unroll
-        for (int g = 0; g < RING - 1; ++g) read_frag(0, g);
+        for (int i = 0; i < MW; ++i) read_a(0, 0, i);
+#pragma unroll
+        for (int g = 0; g < RING - 1; ++g) read_b(0, g);
     }
     using F = std::true_type;
     using T = std::false_type;
-    using E = std::integral_constant<int, 0>;
-    using O = std::integral_constant<int, 1>;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1 % NSET>;
+    using S2 = std::integral_constant<int, 2 % NSET>;
     const int nfull = nkb / KBS;
     int st = 0;
-    if constexpr (DEEP) {   // buffers alternate with the stage parity
-        for (; st + 1 < nfull; st += 2) {
-            run_stage(st, F{}, E{});
-            run_stage(st + 1, F{}, O{});
-        }
-        if (st < nfull) run_stage(st++, F{}, E{});
-        if (st < nst) {
-            if (st & 1) run_stage(st, T{}, O{});
-            else run_stage(st, T{}, E{});
-        }
-    } else {
-        for (; st < nfull; ++st) run_stage(st, F{}, E{});
-        if (st < nst) run_stage(st, T{}, E{});
+    // staging sets rotate with the stage (set st % NSET): unrolled NSET-fold
+    for (; st + NSET <= nfull; st += NSET) {
+        run_stage(st, F{}, S0{});
+        if constexpr (NSET > 1) run_stage(st + 1, F{}, S1{});
+        if constexpr (NSET > 2) run_stage(st + 2, F{}, S2{});
+    }
+    // fewer than NSET full stages left (straight-line: a loop here would make
+    // the compiler copy every register at its back edge), then a short one
+    if (st < nfull) run_stage(st++, F{}, S0{});
+    if constexpr (NSET > 2)
+        if (st < nfull) run_stage(st++, F{}, S1{});
+    if (st < nst) {
+        const int set = st % NSET;
+        if (set == 0) run_stage(st, T{}, S0{});
+        if constexpr (NSET > 1) if (set == 1) run_stage(st, T{}, S1{});
+        if constexpr (NSET > 2) if (set == 2) run_stage(st, T{}, S2{});
     }
 
-    // ---- epilogue straight from the accumulators (an empty K split still
-    // writes its zero partial)
-    const int nlane0 = 4 * f_grp;
+    // ---- epilogue, in MW passes through LDS (the operand ring is free now).
+    // Pass i: every wave parks row block i of its accumulators as int32
+    // (16 rows x 16*NB columns, rows padded by 4 words); then all threads
+    // sweep the 64 parked rows in 16-byte chunks along the rows: whole-line
+    // residual loads and output stores, the fixed epilogue in between.  An
+    // empty K split still writes its zero partial.
+    constexpr int LDR = 16 * NB + 4;   // parked row pitch (int32)
+    constexpr int CH = 4 * NB;         // 16-byte chunks per parked row
+    static_assert(64 * LDR * 4 <= NSLOT * STAGE_BYTES, "epilogue staging fits the ring");
+    static_assert((64 * CH) % PANEL_THREADS == 0, "whole sweep iterations");
+    int32_t* park = reinterpret_cast<int32_t*>(smem);
     const bool vec_ok = (N & 3) == 0 &&
                         (partials || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                                       (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
@@ -345,24 +366,31 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
                                               static_cast<size_t>(N)
                              : nullptr;
     const bool sw_vec = (reinterpret_cast<uintptr_t>(sw) & 15) == 0;
+    __syncthreads();   // every wave is done with the operand ring
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
-        if (i >= mw) continue;
-        const int m = 16 * (rbw + i) + f_row;
-        if (m >= M) continue;
-        const float sxm = part ? 0.0f : sx[m];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            if (j >= ncb) continue;
-            const int n = c0 + 16 * j + nlane0;
-            if (n >= N) continue;
+        for (int j = 0; j < NB; ++j)
+            *reinterpret_cast<i32x4*>(park + (wave * 16 + f_row) * LDR + 16 * j + 4 * (lane >> 4)) = acc[i][j];
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 64 * CH / PANEL_THREADS; ++it) {
+            const int c = t + it * PANEL_THREADS;
+            const int rr = c / CH, cc = c % CH;
+            const int w = rr >> 4, x = rr & 15;
+            const int rbw_w = rs0 + w * nrb / 4;
+            const int mw_w = rs0 + (w + 1) * nrb / 4 - rbw_w;
+            const int m = 16 * (rbw_w + i) + x;
+            const int n = c0 + 4 * cc;
+            if (i >= mw_w || m >= M || 4 * cc >= 16 * ncb || n >= N) continue;
+            const i32x4 a = *reinterpret_cast<const i32x4*>(park + rr * LDR + 4 * cc);
             const size_t o = static_cast<size_t>(m) * static_cast<size_t>(N) + static_cast<size_t>(n);
-            const i32x4 a = acc[i][j];
             if (vec_ok && n + 3 < N) {
                 if (part) {
                     *reinterpret_cast<i32x4*>(part + o) = a;
                     continue;
                 }
+                const float sxm = sx[m];
                 float s0, s1, s2, s3;
                 if (sw_vec) {
                     const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
@@ -389,23 +417,24 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
                 for (int e = 0; e < 4; ++e) {
                     if (n + e >= N) continue;
                     if (part) part[o + e] = a[e];
-                    else y[o + e] = residual ? scale_acc_residual(a[e], sxm, sw[n + e], residual[o + e])
-                                             : scale_acc(a[e], sxm, sw[n + e]);
+                    else y[o + e] = residual ? scale_acc_residual(a[e], sx[m], sw[n + e], residual[o + e])
+                                             : scale_acc(a[e], sx[m], sw[n + e]);
                 }
             }
         }
+        __syncthreads();
     }
 }
 
-// Template configurations (MW row blocks per wave, NB column blocks per
-// panel, DEEP pipeline).  Registers per lane: 4*MW*NB accumulators,
-// 16*MW (32*MW with DEEP) activation, 4*NB (8*NB with DEEP) weight staging
-// and a ring of 4 or 8 weight fragments, within 512.
+// Template configurations: MW row blocks per wave, NB column blocks per
+// panel, NSET staging register sets, NSLOT LDS slots of (64*MW + 16*NB)
+// rows x 128 bytes (within 160 KiB).  Registers per lane: 4*MW*NB
+// accumulators, 4*NSET*(2*MW + NB/2) staging, 8*MW activation and 4 or 8
+// weight fragments, within 512.
 struct PanelKind {
-    int mw, nb;
-    bool deep;
+    int mw, nb, nset, nslot;
 };
-constexpr PanelKind kPanelKinds[] = {{1, 8, true}, {2, 8, true}, {2, 12, true}, {3, 8, true}, {4, 9, false}, {6, 9, false}};
+constexpr PanelKind kPanelKinds[] = {{1, 8, 3, 3}, {2, 8, 3, 3}, {2, 12, 3, 3}, {3, 8, 3, 3}, {4, 9, 3, 3}, {6, 9, 2, 2}};
 constexpr int kNumPanelKinds = sizeof(kPanelKinds) / sizeof(kPanelKinds[0]);
 
 constexpr int NCU = 256;
@@ -413,17 +442,21 @@ constexpr int NCU = 256;
 }  // namespace
 
 // Choose row splits R, column panels P and K splits S <= max_splitk for the
-// panel kernel by a simple time model: the busiest wave's MFMA count, its
-// LDS traffic, HBM bytes (weights once, partials when S > 1) and L2 traffic
-// (every panel reads all activation rows of its K range).  Returns false
-// when no configuration fits (M beyond 4 * 16 * 6 rows per split, etc.).
+// panel kernel with a time model calibrated on MI355X: per round of
+// workgroups, a fixed cost (prologue, the output write, launch) plus, per
+// K-block, the larger of the MFMA issue time (MW*NB products of 16 cycles,
+// times the measured 1.7 for interleaved memory instructions) and the LDS
+// time (fragment reads of 4 waves and the staging writes at 110 B/clk);
+// never below the HBM time of the weights, activations, output and
+// partials; plus the split-K reduction when S > 1.  Returns false when no
+// configuration holds the rows.
 bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, PanelPlan* out) {
     if (M <= 0 || N <= 0 || K <= 0) return false;
     const int64_t rb = (M + 15) / 16, cb = (N + 15) / 16, KB = K / 64;
-    const double f = 2.0e9;         // sustained clock under MFMA load (Hz)
-    const double hbm = 6.0e12;      // sustained HBM bytes/s
-    const double l2 = 20.0e12;      // L2 -> CU bytes/s, whole chip
-    const double lds = 128.0;       // LDS bytes per clock per CU
+    const double f = 1.8e9;          // clock under this kernel's MFMA load (Hz)
+    const double hbm = 5.5e12;       // HBM bytes/s this kernel sustains
+    const double fixed_s = 20e-6;    // per round: prologue, output write, launch
+    const double lds_bpc = 110.0;    // LDS bytes per clock per CU it sustains
     double best = 1e30;
     PanelPlan bp{};
     for (int kind = 0; kind < kNumPanelKinds; ++kind) {
@@ -447,14 +480,15 @@ bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
                 const int64_t rounds = (wgs + NCU - 1) / NCU;
                 const int64_t nkb = std::min<int64_t>(kps, KB);
                 // every wave runs its configuration's full MW x NB products
-                const double mfma_s = static_cast<double>(rounds * MW * NB * nkb) * 16.0 / f;
-                const double lds_s = static_cast<double>(rounds * nkb) * (4.0 * NB + ncb) * 1024.0 / lds / f;
+                const double mfma_cyc = 16.0 * MW * NB * 1.7;
+                const double lds_cyc = (4.0 * (NB + MW) * 1024.0 + (64.0 * MW + 16.0 * NB) * 64.0) / lds_bpc;
+                double t = static_cast<double>(rounds) *
+                           (fixed_s + static_cast<double>(nkb) * std::max(mfma_cyc, lds_cyc) / f);
                 double hbm_bytes = static_cast<double>(N) * K + static_cast<double>(M) * K +
                                    4.0 * M * N * (residual ? 2.0 : 1.0);
-                if (S > 1) hbm_bytes += 8.0 * S * M * N;
-                const double l2_bytes = static_cast<double>(P) * M * K + static_cast<double>(R) * N * K;
-                double t = std::max(std::max(mfma_s, lds_s), std::max(hbm_bytes / hbm, l2_bytes / l2));
-                t += 3.0e-6 * (S > 1 ? 1 : 0);   // second launch
+                if (S > 1) hbm_bytes += 4.0 * S * M * N;
+                t = std::max(t, hbm_bytes / hbm + 8e-6);
+                if (S > 1) t += 3e-6 + (4.0 * S + 8.0) * M * N / 4.0e12;   // reduction kernel
                 if (t < best * 0.999) {
                     best = t;
                     bp.kind = kind;
@@ -474,7 +508,7 @@ bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
 
 namespace {
 
-template <int MW, int NB, bool DEEP>
+template <int MW, int NB, int NSET, int NSLOT>
 hipError_t launch_panel_t(const GemmArgs& a, const PanelPlan& p, int32_t* partials, hipStream_t stream) {
     const int64_t cb = (a.N + 15) / 16;
     PanelParams pp;
@@ -489,17 +523,19 @@ hipError_t launch_panel_t(const GemmArgs& a, const PanelPlan& p, int32_t* partia
     pp.S = p.S;
     pp.kb_per_split = p.kb_per_split;
     const unsigned nblocks = static_cast<unsigned>(static_cast<int64_t>(p.P) * p.R * p.S);
-    hipLaunchKernelGGL((gemm_panel<MW, NB, DEEP>), dim3(nblocks), dim3(PANEL_THREADS), 0, stream, a.xq, a.sx,
+    hipLaunchKernelGGL((gemm_panel<MW, NB, NSET, NSLOT>), dim3(nblocks), dim3(PANEL_THREADS), 0, stream, a.xq, a.sx,
                        a.w, a.sw, a.residual, a.y, partials, pp);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool panel_kind_shape(int kind, int* mw, int* nb) {
+bool panel_kind_shape(int kind, int* mw, int* nb, int* nset, int* nslot) {
     if (kind < 0 || kind >= kNumPanelKinds) return false;
     *mw = kPanelKinds[kind].mw;
     *nb = kPanelKinds[kind].nb;
+    *nset = kPanelKinds[kind].nset;
+    *nslot = kPanelKinds[kind].nslot;
     return true;
 }
 
@@ -522,12 +558,12 @@ hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, 
     if (a.acc_out && p.S > 1) return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (p.kind) {
-        case 0: e = launch_panel_t<1, 8, true>(a, p, partials, stream); break;
-        case 1: e = launch_panel_t<2, 8, true>(a, p, partials, stream); break;
-        case 2: e = launch_panel_t<2, 12, true>(a, p, partials, stream); break;
-        case 3: e = launch_panel_t<3, 8, true>(a, p, partials, stream); break;
-        case 4: e = launch_panel_t<4, 9, false>(a, p, partials, stream); break;
-        case 5: e = launch_panel_t<6, 9, false>(a, p, partials, stream); break;
+        case 0: e = launch_panel_t<1, 8, 3, 3>(a, p, partials, stream); break;
+        case 1: e = launch_panel_t<2, 8, 3, 3>(a, p, partials, stream); break;
+        case 2: e = launch_panel_t<2, 12, 3, 3>(a, p, partials, stream); break;
+        case 3: e = launch_panel_t<3, 8, 3, 3>(a, p, partials, stream); break;
+        case 4: e = launch_panel_t<4, 9, 3, 3>(a, p, partials, stream); break;
+        case 5: e = launch_panel_t<6, 9, 2, 2>(a, p, partials, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || p.S <= 1 || a.acc_out) return e;

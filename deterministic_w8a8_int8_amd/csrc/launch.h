@@ -82,8 +82,9 @@ struct PanelPlan {
 };
 bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, PanelPlan* out);
 bool panel_plan_valid(int64_t M, int64_t N, int64_t K, const PanelPlan& p);
-// Rows-per-wave and columns-per-panel limits (in blocks of 16) of a panel kind.
-bool panel_kind_shape(int kind, int* mw, int* nb);
+// Rows-per-wave and columns-per-panel limits (in blocks of 16), staging
+// register sets and LDS slots of a panel kind.
+bool panel_kind_shape(int kind, int* mw, int* nb, int* nset, int* nslot);
 hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, hipStream_t stream);
 
 // Skinny-M GEMM (M <= SKINNY_MAX_M): the weight is streamed from HBM once and

@@ -85,15 +85,15 @@ int w8a8_set_tile_override(int kind);
 /*
  * Diagnostic (host, no GPU call): which kernel w8a8_gemm_splitk would run
  * for this shape, split bound and residual flag (w8a8_gemm is splitk 1),
- * under the current tile override.  out: host int32[8], filled as
+ * under the current tile override.  out: host int32[10], filled as
  *   out[0] = 0: skinny kernel (M <= 64); rest 0.
  *   out[0] = 1: tiled kernel; out[1] tile configuration, out[2] and out[3]
- *            the tile's rows and columns, out[4] the K splits.
+ *            the tile's rows and columns, out[4] the K splits; rest 0.
  *   out[0] = 2: column-panel kernel; out[1] its configuration, out[2] row
  *            splits R, out[3] column panels P, out[4] K splits S (at most
  *            splitk), out[5] 64-byte K-blocks per split, out[6] row blocks
  *            of 16 per wave (limit), out[7] column blocks of 16 per panel
- *            (limit).
+ *            (limit), out[8] staging register sets, out[9] LDS slots.
  * Returns W8A8_ERR_INVALID_ARG for an invalid shape or a NULL out.
  */
 int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, int32_t* out);

@@ -17,7 +17,8 @@ import pytest
 
 from deterministic_w8a8_int8_amd import binding as B
 
-NXCD, KBS, NSTB, ROW_BYTES = 8, 4, 3, 256
+NXCD, KBS, ROW_BYTES, THREADS, LDS_LIMIT = 8, 2, 128, 256, 160 * 1024
+OUT_OF_RANGE = 0x40000000
 
 
 def block_map(nblocks):
@@ -31,17 +32,33 @@ def block_map(nblocks):
     return lids
 
 
+def swz(r):
+    return (r & 7) ^ ((r >> 3) & 1)
+
+
 def check_plan(M, N, K, plan):
-    path, kind, R, P, S, kps, MW, NB = plan
+    path, kind, R, P, S, kps, MW, NB, NSET, NSLOT = plan
     assert path == 2
+    assert NSLOT in (2, 3) and NSET >= NSLOT - 1
     rb_total, cb, KB = -(-M // 16), -(-N // 16), K // 64
     cb_base, cb_extra = divmod(cb, P)
+    AR, BR = 64 * MW, 16 * NB
+    RPAD = (AR + BR + 31) // 32 * 32
+    QPT, QA = RPAD // 32, AR // 32
+    STAGE = RPAD * ROW_BYTES
+    assert NSLOT * STAGE <= LDS_LIMIT, "LDS ring"
+    LDR = 16 * NB + 4
+    assert 64 * LDR * 4 <= NSLOT * STAGE, "epilogue parking fits the ring"
+    assert (64 * 4 * NB) % THREADS == 0
+    assert 4 * MW * NB <= 256, "accumulators"
     nblocks = P * R * S
     lids = block_map(nblocks)
     assert sorted(lids) == list(range(nblocks)), "block renumbering is not a permutation"
     cover = np.zeros((S, rb_total, cb), dtype=np.int32)
     kcover = np.zeros(KB, dtype=np.int32)
-    lds_bytes = NSTB * NB * 16 * ROW_BYTES
+    t = np.arange(THREADS)
+    st_lc = (t & 7) ^ swz(t >> 3)
+    lane = np.arange(64)
     for lid in lids:
         r, split, p = lid % R, (lid // R) % S, lid // (R * S)
         assert p < P
@@ -56,42 +73,57 @@ def check_plan(M, N, K, plan):
             kcover[kb0:kb0 + nkb] += 1
         rs0, rs1 = r * rb_total // R, (r + 1) * rb_total // R
         nrb = rs1 - rs0
+        assert nrb >= 1
+        row_end, row_first = min(16 * rs1, M), min(16 * rs0, M - 1)
+        a_range, b_range = (row_end - row_first) * K, (min(c0 + BR, N) - c0) * K
+        assert 0 < a_range < 2 ** 31 and 0 < b_range < 2 ** 31
         for wave in range(4):
             rbw = rs0 + wave * nrb // 4
             mw = rs0 + (wave + 1) * nrb // 4 - rbw
             assert 0 <= mw <= MW, (mw, MW)
             cover[split, rbw:rbw + mw, cb0:cb0 + ncb] += 1
-            # activation fragments: rows clamped to M-1, bytes 64*kb + 16*grp .. +16
-            for i in range(mw):
-                rows = np.minimum(16 * (rbw + i) + np.arange(16), M - 1)
-                assert rows.min() >= 0 and rows.max() < M
-            if nkb:
-                assert (kb0 + nkb - 1) * 64 + 48 + 16 <= K
-        # weight staging: thread t, row t/16 + 16q (clamped), logical chunk lc
-        t = np.arange(256)
-        st_lc = (t & 15) ^ (t >> 4)
-        for st in range(nst):
-            kin = nkb - st * KBS
-            lc = np.where((st_lc >> 2) < kin, st_lc, st_lc & 3)
-            kbyte = kb0 * 64 + st * ROW_BYTES + lc * 16
-            assert kbyte.min() >= 0 and (kbyte + 16).max() <= K
-            # the chunk's K-block lies inside this split whenever it is multiplied
-            used = (lc >> 2) < min(kin, KBS)
-            assert ((kbyte[used] >> 6) < kb0 + nkb).all()
-        for q in range(ncb):
-            col = np.minimum(c0 + 16 * q + (t >> 4), N - 1)
-            assert col.max() < N
-            assert (col - c0).max() * K < 2 ** 32
-            # LDS store and fragment-read offsets inside the ring
-            assert (NSTB - 1) * NB * 16 * ROW_BYTES + 16 * 255 + q * 16 * ROW_BYTES + 16 <= lds_bytes
-        lane = np.arange(64)
+        # staging loads: every in-range offset stays inside its buffer for every stage
+        for q in range(QPT):
+            sr = (t >> 3) + 32 * q
+            if q < QA:
+                w, x = sr // (16 * MW), sr % (16 * MW)
+                rbw_w = rs0 + w * nrb // 4
+                mw_w = rs0 + (w + 1) * nrb // 4 - rbw_w
+                row = np.minimum(16 * rbw_w + x, row_end - 1)
+                own = (x < 16 * mw_w) & (16 * rbw_w + x < row_end)
+                off = np.where(own, (row - row_first) * K + st_lc * 16, OUT_OF_RANGE)
+                rng = a_range
+            else:
+                br = sr - AR
+                col = np.minimum(c0 + br, N - 1)
+                own = (br < 16 * ncb) & (c0 + br < N)
+                off = np.where(own, (col - c0) * K + st_lc * 16, OUT_OF_RANGE)
+                rng = b_range
+            for st in {0, max(nst - 1, 0)}:
+                if nst == 0:
+                    break
+                lcd = np.where((st_lc >> 2) < nkb - st * KBS, 0, -64)
+                soff = (kb0 + st * KBS) * 64
+                full = off + lcd + soff
+                inb = off != OUT_OF_RANGE
+                assert (full[inb] >= 0).all() and (full[inb] + 16 <= rng).all(), (q, st)
+                assert (full[~inb] >= rng).all() and (full[~inb] + 16 < 2 ** 31).all()
+                # a multiplied chunk (its K-block inside the stage) belongs to this split
+                used = inb & ((st_lc >> 2) < min(nkb - st * KBS, KBS))
+                kbyte = (full[used] - st_lc[used] * 16 - lcd[used]) % K + st_lc[used] * 16 + lcd[used]
+                assert ((kbyte >> 6) >= kb0).all() and ((kbyte >> 6) < kb0 + nkb).all()
+            # LDS store offset of piece q inside the ring
+            assert (NSLOT - 1) * STAGE + 16 * t.max() + q * 32 * ROW_BYTES + 16 <= NSLOT * STAGE
+        # fragment reads inside the ring; 16 lanes of a read hit 16 distinct 16-byte bank groups
         for u in range(KBS):
-            f_off = (lane & 15) * ROW_BYTES + (((4 * u + (lane >> 4)) ^ (lane & 15)) * 16)
-            assert f_off.max() + (ncb - 1) * 16 * ROW_BYTES + (NSTB - 1) * NB * 16 * ROW_BYTES + 16 <= lds_bytes
-            # bank spread: 16 lanes of one read phase hit 16 distinct 16-byte slots of 256 bytes
+            f_off = (lane & 15) * ROW_BYTES + (((4 * u + (lane >> 4)) ^ swz(lane & 15)) * 16)
+            top_a = 3 * 16 * MW * ROW_BYTES + 16 * (MW - 1) * ROW_BYTES + f_off.max() + 16
+            top_b = (AR + 16 * (NB - 1)) * ROW_BYTES + f_off.max() + 16
+            assert max(top_a, top_b) <= STAGE
             for ph in range(4):
-                slots = (f_off[16 * ph:16 * ph + 16] % 256) // 16
-                assert len(set(slots.tolist())) == 16
+                b = ((lane[16 * ph:16 * ph + 16] & 15) * ROW_BYTES + f_off[16 * ph:16 * ph + 16] % ROW_BYTES)
+                groups = (b % 256) // 16
+                assert len(set(groups.tolist())) == 16
     assert (kcover == 1).all(), "K splits must tile the K-blocks exactly once"
     assert (cover == 1).all(), "every (row block, column block) once per K split"
 
