@@ -186,18 +186,20 @@ int w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* s
 size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splitk);
 
 /*
- * w8a8_gemm_splitk -- the same result as w8a8_gemm, with K cut into
- * `splitk` contiguous chunks (review page, section "Bitwise consistency is
- * not lossless quantization": split-K partial sums stay integers).
- *     chunk c covers k in [c*Kc, min((c+1)*Kc, K)), Kc = ceil(K/splitk)
- *     rounded up to a multiple of 64;
+ * w8a8_gemm_splitk -- the same result as w8a8_gemm, with K cut into at
+ * most `splitk` contiguous chunks (review page, section "Bitwise
+ * consistency is not lossless quantization": split-K partial sums stay
+ * integers).  With S chunks (S = splitk for M > 512; for 64 < M <= 512 the
+ * column-panel kernel picks S <= splitk for speed, see w8a8_gemm_plan):
+ *     chunk c covers k in [c*Kc, min((c+1)*Kc, K)), Kc = ceil(K/S)
+ *     rounded up to a multiple of 64 (of 128 on the panel kernel);
  *     P_c[m,n] = sum over chunk c of xq[m,k]*w[n,k]      (int32)
- *     acc      = P_0 + P_1 + ... + P_{splitk-1}           (int32)
+ *     acc      = P_0 + P_1 + ... + P_{S-1}                (int32)
  * followed by the same epilogue as w8a8_gemm.  No floating-point atomic is
  * used anywhere.  Each chunk writes P_c as int32 to its own slice of the
  * workspace; a second kernel on the same stream adds the slices in chunk
  * order and runs the epilogue.  Integer addition is exact and associative,
- * so neither that order nor splitk can change a bit: the output is
+ * so neither that order nor S can change a bit: the output is
  * bit-identical to w8a8_gemm.
  *
  * splitk     1 <= splitk <= W8A8_MAX_SPLITK.
