@@ -27,6 +27,7 @@ W8A8_ERR_HIP = -7
 W8A8_MAX_K = 133120
 W8A8_MAX_CANDIDATES = 64
 W8A8_MAX_SPLITK = 64
+W8A8_TILE_OVERRIDE_PANEL = 7
 
 # Every symbol include/w8a8.h declares, with its ctypes signature.
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t

@@ -86,12 +86,13 @@ struct Cfg {
     static constexpr int ACC_PER_WAVE = WTM * WTN * 16 * 64;  // int32 per wave
     static constexpr int STAGED_ROWS = 32 * WGM;      // epilogue rows per pass
     static constexpr int LDR = BN + 4;                // staged row pitch (int32), 4 mod 64 banks
-    static constexpr int EPI_BYTES = STAGED_ROWS * LDR * 4 + (BM + BN) * 4;
+    static constexpr int EPI_BYTES = DIRECT_EPI ? 0 : STAGED_ROWS * LDR * 4 + (BM + BN) * 4;
     static constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
     static_assert(A_LOADS * ROWS_PER_FILL * NW == BM && B_LOADS * ROWS_PER_FILL * NW == BN,
                   "fills must cover the tile");
     static_assert(NST >= 2 && NST <= 4, "pipeline depth");
-    static_assert(THREADS % (BN / 4) == 0, "epilogue sweep");
+    static_assert(DIRECT_EPI || THREADS % (BN / 4) == 0, "epilogue sweep");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
 };
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -445,21 +446,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
         const bool vec_ok = (N & 3) == 0 &&
                             (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                                       (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
-        float swv[WTN][16];
+        // Weight scales are loaded per column fragment (16 per lane) so that
+        // wide tiles do not hold WTN x 16 of them beside the accumulators.
 #pragma unroll
-        for (int j = 0; j < WTN; ++j)
+        for (int j = 0; j < WTN; ++j) {
+            float swv[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int col = col0 + wn * 32 * WTN + j * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                swv[j][e] = part ? 0.0f : sw[min(col, N - 1)];
+                swv[e] = part ? 0.0f : sw[min(col, N - 1)];
             }
 #pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-            const int row = row0 + wm * 32 * WTM + i * 32 + (lane & 31);
-            if (row >= M) continue;
-            const float sxm = part ? 0.0f : sx[row];
-#pragma unroll
-            for (int j = 0; j < WTN; ++j) {
+            for (int i = 0; i < WTM; ++i) {
+                const int row = row0 + wm * 32 * WTM + i * 32 + (lane & 31);
+                if (row >= M) continue;
+                const float sxm = part ? 0.0f : sx[row];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int col = col0 + wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
@@ -474,15 +475,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                         float4 v;
                         if (residual) {
                             const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
-                            v.x = scale_acc_residual(a[0], sxm, swv[j][4 * g], r4.x);
-                            v.y = scale_acc_residual(a[1], sxm, swv[j][4 * g + 1], r4.y);
-                            v.z = scale_acc_residual(a[2], sxm, swv[j][4 * g + 2], r4.z);
-                            v.w = scale_acc_residual(a[3], sxm, swv[j][4 * g + 3], r4.w);
+                            v.x = scale_acc_residual(a[0], sxm, swv[4 * g], r4.x);
+                            v.y = scale_acc_residual(a[1], sxm, swv[4 * g + 1], r4.y);
+                            v.z = scale_acc_residual(a[2], sxm, swv[4 * g + 2], r4.z);
+                            v.w = scale_acc_residual(a[3], sxm, swv[4 * g + 3], r4.w);
                         } else {
-                            v.x = scale_acc(a[0], sxm, swv[j][4 * g]);
-                            v.y = scale_acc(a[1], sxm, swv[j][4 * g + 1]);
-                            v.z = scale_acc(a[2], sxm, swv[j][4 * g + 2]);
-                            v.w = scale_acc(a[3], sxm, swv[j][4 * g + 3]);
+                            v.x = scale_acc(a[0], sxm, swv[4 * g]);
+                            v.y = scale_acc(a[1], sxm, swv[4 * g + 1]);
+                            v.z = scale_acc(a[2], sxm, swv[4 * g + 2]);
+                            v.w = scale_acc(a[3], sxm, swv[4 * g + 3]);
                         }
                         *reinterpret_cast<float4*>(y + o) = v;
                     } else {
@@ -490,150 +491,149 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                         for (int q = 0; q < 4; ++q) {
                             if (col + q >= N) continue;
                             if (part) part[o + q] = a[q];
-                            else y[o + q] = residual ? scale_acc_residual(a[q], sxm, swv[j][4 * g + q], residual[o + q])
-                                                     : scale_acc(a[q], sxm, swv[j][4 * g + q]);
+                            else y[o + q] = residual ? scale_acc_residual(a[q], sxm, swv[4 * g + q], residual[o + q])
+                                                     : scale_acc(a[q], sxm, swv[4 * g + q]);
                         }
                     }
                 }
                 sched_fence();
             }
         }
-        return;
-    }
-
-    // ---- epilogue, in WTM passes of STAGED_ROWS rows.  Every wave parks one
-    // 32-row slice of its accumulators in LDS (row-major int32, four adjacent
-    // columns per 16-byte write; rows padded by 4 words so that the 16 lanes
-    // of one write phase, 16 different rows, hit 16 different bank groups).
-    // Then all threads sweep the slice in float4 chunks along rows, one
-    // 16-byte residual load and one 16-byte output store per chunk, fully
-    // coalesced.
-    constexpr int LDR = C::LDR;
-    int32_t* stage = reinterpret_cast<int32_t*>(smem);
-    float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
-    float* s_sw = s_sx + C::BM;
-    __syncthreads();  // all waves are done reading the operand buffers
-    if (!part) {   // raw int32 output reads no scales
-        for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
-        for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
-    }
-
-    // (a partial slice starts 16-byte aligned whenever N % 4 == 0: the
-    // workspace is 256-byte aligned)
-    const bool vec_ok = (N & 3) == 0 &&
-                        (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
-                                  (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
-    constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
-    constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
-    constexpr int RPT = C::STAGED_ROWS / ROWS_PER_SWEEP;   // staged rows per thread
-    static_assert(C::STAGED_ROWS % ROWS_PER_SWEEP == 0, "epilogue sweep");
-    const int c4 = threadIdx.x % C4;
-    const int rsub = threadIdx.x / C4;
-    const int col = col0 + 4 * c4;
-    // Interior tile with aligned rows: a straight-line sweep, every LDS read
-    // issued before the first store.  Otherwise the checked loop below.
-    const bool fast = vec_ok && row0 + C::BM <= M && col0 + C::BN <= N;
-#pragma unroll
-    for (int pass = 0; pass < WTM; ++pass) {
-        // accumulator slice i = pass of every wave -> staged rows wm*32 + r
-        const int lr = wm * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int lc = wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) =
-                    i32x4{acc[pass][j][4 * g], acc[pass][j][4 * g + 1], acc[pass][j][4 * g + 2],
-                          acc[pass][j][4 * g + 3]};
-            }
-            sched_fence();
+    } else {
+        // ---- epilogue, in WTM passes of STAGED_ROWS rows.  Every wave parks one
+        // 32-row slice of its accumulators in LDS (row-major int32, four adjacent
+        // columns per 16-byte write; rows padded by 4 words so that the 16 lanes
+        // of one write phase, 16 different rows, hit 16 different bank groups).
+        // Then all threads sweep the slice in float4 chunks along rows, one
+        // 16-byte residual load and one 16-byte output store per chunk, fully
+        // coalesced.
+        constexpr int LDR = C::LDR;
+        int32_t* stage = reinterpret_cast<int32_t*>(smem);
+        float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
+        float* s_sw = s_sx + C::BM;
+        __syncthreads();  // all waves are done reading the operand buffers
+        if (!part) {   // raw int32 output reads no scales
+            for (int t = threadIdx.x; t < C::BM; t += C::THREADS) s_sx[t] = sx[min(row0 + t, M - 1)];
+            for (int t = threadIdx.x; t < C::BN; t += C::THREADS) s_sw[t] = sw[min(col0 + t, N - 1)];
         }
-        __syncthreads();
-        const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
-        if (fast) {
-            // staged row r = rsub + k * ROWS_PER_SWEEP is tile row
-            // (r / 32) * 32 * WTM + pass * 32 + r % 32
-            i32x4 av[RPT];
-            float sxv[RPT];
-            size_t ov[RPT];
-#pragma unroll
-            for (int k = 0; k < RPT; ++k) {
-                const int r = rsub + k * ROWS_PER_SWEEP;
-                const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
-                av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
-                sxv[k] = s_sx[lr];
-                ov[k] = static_cast<size_t>(row0 + lr) * N + col;
-            }
-            if (part) {
-#pragma unroll
-                for (int k = 0; k < RPT; ++k) *reinterpret_cast<i32x4*>(part + ov[k]) = av[k];
-            } else if (residual) {
-                float4 rv[RPT];
-#pragma unroll
-                for (int k = 0; k < RPT; ++k) rv[k] = *reinterpret_cast<const float4*>(residual + ov[k]);
-#pragma unroll
-                for (int k = 0; k < RPT; ++k) {
-                    float4 v;
-                    v.x = scale_acc_residual(av[k][0], sxv[k], sw4.x, rv[k].x);
-                    v.y = scale_acc_residual(av[k][1], sxv[k], sw4.y, rv[k].y);
-                    v.z = scale_acc_residual(av[k][2], sxv[k], sw4.z, rv[k].z);
-                    v.w = scale_acc_residual(av[k][3], sxv[k], sw4.w, rv[k].w);
-                    *reinterpret_cast<float4*>(y + ov[k]) = v;
+
+        // (a partial slice starts 16-byte aligned whenever N % 4 == 0: the
+        // workspace is 256-byte aligned)
+        const bool vec_ok = (N & 3) == 0 &&
+                            (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                                      (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
+        constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
+        constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
+        constexpr int RPT = C::STAGED_ROWS / ROWS_PER_SWEEP;   // staged rows per thread
+        static_assert(C::STAGED_ROWS % ROWS_PER_SWEEP == 0, "epilogue sweep");
+        const int c4 = threadIdx.x % C4;
+        const int rsub = threadIdx.x / C4;
+        const int col = col0 + 4 * c4;
+        // Interior tile with aligned rows: a straight-line sweep, every LDS read
+        // issued before the first store.  Otherwise the checked loop below.
+        const bool fast = vec_ok && row0 + C::BM <= M && col0 + C::BN <= N;
+    #pragma unroll
+        for (int pass = 0; pass < WTM; ++pass) {
+            // accumulator slice i = pass of every wave -> staged rows wm*32 + r
+            const int lr = wm * 32 + (lane & 31);
+    #pragma unroll
+            for (int j = 0; j < WTN; ++j) {
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int lc = wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                    *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) =
+                        i32x4{acc[pass][j][4 * g], acc[pass][j][4 * g + 1], acc[pass][j][4 * g + 2],
+                              acc[pass][j][4 * g + 3]};
                 }
-            } else {
-#pragma unroll
+                sched_fence();
+            }
+            __syncthreads();
+            const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
+            if (fast) {
+                // staged row r = rsub + k * ROWS_PER_SWEEP is tile row
+                // (r / 32) * 32 * WTM + pass * 32 + r % 32
+                i32x4 av[RPT];
+                float sxv[RPT];
+                size_t ov[RPT];
+    #pragma unroll
                 for (int k = 0; k < RPT; ++k) {
+                    const int r = rsub + k * ROWS_PER_SWEEP;
+                    const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
+                    av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
+                    sxv[k] = s_sx[lr];
+                    ov[k] = static_cast<size_t>(row0 + lr) * N + col;
+                }
+                if (part) {
+    #pragma unroll
+                    for (int k = 0; k < RPT; ++k) *reinterpret_cast<i32x4*>(part + ov[k]) = av[k];
+                } else if (residual) {
+                    float4 rv[RPT];
+    #pragma unroll
+                    for (int k = 0; k < RPT; ++k) rv[k] = *reinterpret_cast<const float4*>(residual + ov[k]);
+    #pragma unroll
+                    for (int k = 0; k < RPT; ++k) {
+                        float4 v;
+                        v.x = scale_acc_residual(av[k][0], sxv[k], sw4.x, rv[k].x);
+                        v.y = scale_acc_residual(av[k][1], sxv[k], sw4.y, rv[k].y);
+                        v.z = scale_acc_residual(av[k][2], sxv[k], sw4.z, rv[k].z);
+                        v.w = scale_acc_residual(av[k][3], sxv[k], sw4.w, rv[k].w);
+                        *reinterpret_cast<float4*>(y + ov[k]) = v;
+                    }
+                } else {
+    #pragma unroll
+                    for (int k = 0; k < RPT; ++k) {
+                        float4 v;
+                        v.x = scale_acc(av[k][0], sxv[k], sw4.x);
+                        v.y = scale_acc(av[k][1], sxv[k], sw4.y);
+                        v.z = scale_acc(av[k][2], sxv[k], sw4.z);
+                        v.w = scale_acc(av[k][3], sxv[k], sw4.w);
+                        *reinterpret_cast<float4*>(y + ov[k]) = v;
+                    }
+                }
+                __syncthreads();
+                continue;
+            }
+            for (int r = rsub; r < C::STAGED_ROWS; r += ROWS_PER_SWEEP) {
+                // staged row r is tile row (r / 32) * 32 * WTM + pass * 32 + r % 32
+                const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
+                const int row = row0 + lr;
+                if (row >= M) continue;
+                const int4 a4 = *reinterpret_cast<const int4*>(stage + r * LDR + 4 * c4);
+                const float sxm = s_sx[lr];
+                const size_t o = static_cast<size_t>(row) * N + col;
+                if (vec_ok && col + 3 < N) {
+                    if (part) {
+                        *reinterpret_cast<int4*>(part + o) = a4;
+                        continue;
+                    }
                     float4 v;
-                    v.x = scale_acc(av[k][0], sxv[k], sw4.x);
-                    v.y = scale_acc(av[k][1], sxv[k], sw4.y);
-                    v.z = scale_acc(av[k][2], sxv[k], sw4.z);
-                    v.w = scale_acc(av[k][3], sxv[k], sw4.w);
-                    *reinterpret_cast<float4*>(y + ov[k]) = v;
+                    if (residual) {
+                        const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
+                        v.x = scale_acc_residual(a4.x, sxm, sw4.x, r4.x);
+                        v.y = scale_acc_residual(a4.y, sxm, sw4.y, r4.y);
+                        v.z = scale_acc_residual(a4.z, sxm, sw4.z, r4.z);
+                        v.w = scale_acc_residual(a4.w, sxm, sw4.w, r4.w);
+                    } else {
+                        v.x = scale_acc(a4.x, sxm, sw4.x);
+                        v.y = scale_acc(a4.y, sxm, sw4.y);
+                        v.z = scale_acc(a4.z, sxm, sw4.z);
+                        v.w = scale_acc(a4.w, sxm, sw4.w);
+                    }
+                    *reinterpret_cast<float4*>(y + o) = v;
+                } else {
+                    const int32_t av[4] = {a4.x, a4.y, a4.z, a4.w};
+                    const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (col + q >= N) continue;
+                        if (part) part[o + q] = av[q];
+                        else y[o + q] = residual ? scale_acc_residual(av[q], sxm, swv[q], residual[o + q])
+                                                 : scale_acc(av[q], sxm, swv[q]);
+                    }
                 }
             }
             __syncthreads();
-            continue;
         }
-        for (int r = rsub; r < C::STAGED_ROWS; r += ROWS_PER_SWEEP) {
-            // staged row r is tile row (r / 32) * 32 * WTM + pass * 32 + r % 32
-            const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
-            const int row = row0 + lr;
-            if (row >= M) continue;
-            const int4 a4 = *reinterpret_cast<const int4*>(stage + r * LDR + 4 * c4);
-            const float sxm = s_sx[lr];
-            const size_t o = static_cast<size_t>(row) * N + col;
-            if (vec_ok && col + 3 < N) {
-                if (part) {
-                    *reinterpret_cast<int4*>(part + o) = a4;
-                    continue;
-                }
-                float4 v;
-                if (residual) {
-                    const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
-                    v.x = scale_acc_residual(a4.x, sxm, sw4.x, r4.x);
-                    v.y = scale_acc_residual(a4.y, sxm, sw4.y, r4.y);
-                    v.z = scale_acc_residual(a4.z, sxm, sw4.z, r4.z);
-                    v.w = scale_acc_residual(a4.w, sxm, sw4.w, r4.w);
-                } else {
-                    v.x = scale_acc(a4.x, sxm, sw4.x);
-                    v.y = scale_acc(a4.y, sxm, sw4.y);
-                    v.z = scale_acc(a4.z, sxm, sw4.z);
-                    v.w = scale_acc(a4.w, sxm, sw4.w);
-                }
-                *reinterpret_cast<float4*>(y + o) = v;
-            } else {
-                const int32_t av[4] = {a4.x, a4.y, a4.z, a4.w};
-                const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (col + q >= N) continue;
-                    if (part) part[o + q] = av[q];
-                    else y[o + q] = residual ? scale_acc_residual(av[q], sxm, swv[q], residual[o + q])
-                                             : scale_acc(av[q], sxm, swv[q]);
-                }
-            }
-        }
-        __syncthreads();
     }
 }
 
@@ -721,6 +721,10 @@ using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per 
 using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU
 using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1>;  // 256x256, 8 waves, 128-byte stages x2
 using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true>;  // as 4, epilogue stored from the accumulators
+// 256x320, 8 waves of 64x160, 128-byte stages x2, epilogue from the
+// accumulators: N = 5120 is 16 such tiles, so M = 8192 makes 512 tiles, two
+// full rounds on 256 CUs where 256x256 tiles make 2.5
+using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, true>;
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {
@@ -751,6 +755,7 @@ const KindInfo kKinds[TILE_KINDS] = {
     {Cfg3::BM, Cfg3::BN, Cfg3::OCC, 0.70},
     {Cfg4::BM, Cfg4::BN, Cfg4::OCC, 1.00},
     {Cfg5::BM, Cfg5::BN, Cfg5::OCC, 0.97},
+    {Cfg6::BM, Cfg6::BN, Cfg6::OCC, 0.97},
 };
 
 int tile_override = -1;
@@ -810,6 +815,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, void* workspa
         case 3: return launch_cfg<Cfg3>(a, p, workspace, stream);
         case 4: return launch_cfg<Cfg4>(a, p, workspace, stream);
         case 5: return launch_cfg<Cfg5>(a, p, workspace, stream);
+        case 6: return launch_cfg<Cfg6>(a, p, workspace, stream);
         default: break;
     }
     return hipErrorInvalidValue;

@@ -64,6 +64,8 @@ typedef enum {
 #define W8A8_MAX_CANDIDATES 64
 /* Largest split-K factor accepted. */
 #define W8A8_MAX_SPLITK 64
+/* w8a8_set_tile_override value that forces the column-panel kernel. */
+#define W8A8_TILE_OVERRIDE_PANEL 7
 
 /* Human-readable name of a status code (host; never NULL). */
 const char* w8a8_status_string(int status);
@@ -76,9 +78,11 @@ int w8a8_abi_version(void);
  * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
  * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
  * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
- * stages, 5: as 4 with the epilogue stored straight from the accumulators);
- * 6 forces the column-panel kernel wherever it can hold the rows (by default
- * it runs for 64 < M <= 512).  It never changes a result bit, only speed.
+ * stages, 5: as 4 with the epilogue stored straight from the accumulators,
+ * 6: 256x320 with 8 waves and the epilogue from the accumulators);
+ * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
+ * hold the rows (by default it runs for 64 < M <= 512).  It never changes a
+ * result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */
 int w8a8_set_tile_override(int kind);
 

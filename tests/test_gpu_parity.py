@@ -156,7 +156,7 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_every_tile_shape_gives_identical_bits(kind):
     M, N, K = 300, 520, 704
     say(f"tile kind {kind}")
@@ -201,7 +201,7 @@ def test_panel_kernel_matches_oracle(M, N, K):
     want_r = oracle.gemm(xq, sx, w, sw, r)
     want = oracle.gemm(xq, sx, w, sw)
     d = [dev(xq), dev(sx), dev(w), dev(sw)]
-    B.set_tile_override(6)
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_PANEL)
     try:
         got = host(B.w8a8_gemm(*d))
         got_r = host(B.w8a8_gemm(*d, residual=dev(r)))

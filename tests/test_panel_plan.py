@@ -148,7 +148,7 @@ def test_panel_plan_in_bounds(M, N, K, S, res):
 
 def test_panel_plan_forced_small_and_ragged():
     """With the panel kernel forced, small and ragged shapes still plan in bounds."""
-    B.set_tile_override(6)
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_PANEL)
     try:
         for M, N, K, S in itertools.product([1, 15, 16, 17, 63, 64, 200], [1, 15, 17, 300], [64, 192, 1024], [1, 3]):
             plan = B.w8a8_gemm_plan(M, N, K, S, 0)
@@ -167,7 +167,7 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 1
-    for kind in range(6):
+    for kind in range(7):
         B.set_tile_override(kind)
         try:
             assert B.w8a8_gemm_plan(256, 34816, 5120, 1, 0)[0] == 1
