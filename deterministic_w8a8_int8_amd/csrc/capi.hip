@@ -74,8 +74,10 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 }
 
 // The panel kernel takes M in (SKINNY_MAX_M, kPanelMaxM] unless the override
-// forces a tiled configuration (0..5) or the panel kernel (6, any M it fits).
+// forces a tiled configuration (0..TILE_KINDS-1) or the panel kernel
+// (PANEL_OVERRIDE, any M it fits).
 constexpr int64_t kPanelMaxM = 512;
+static_assert(W8A8_TILE_OVERRIDE_PANEL == w8a8::PANEL_OVERRIDE, "header and library disagree on the panel override");
 
 bool pick_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, w8a8::PanelPlan* pp) {
     const int ov = w8a8::tile_override_value();

@@ -141,3 +141,14 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_probe_stream_read(p, 0, p, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_stream_read(p, 1024, nul, S) == B.W8A8_ERR_INVALID_ARG
     del keep
+
+
+def test_binding_constants_match_the_header():
+    """Every integer #define and status code of the header has the same value in the binding."""
+    from deterministic_w8a8_int8_amd import binding
+    text = open(HEADER).read()
+    pairs = re.findall(r"#define\s+(W8A8_[A-Z0-9_]+)\s+(-?\d+)", text)
+    pairs += re.findall(r"\b(W8A8_(?:OK|ERR_[A-Z_]+))\s*=\s*(-?\d+)", text)
+    assert len(pairs) >= 12
+    for name, value in pairs:
+        assert getattr(binding, name) == int(value), name

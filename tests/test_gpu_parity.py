@@ -156,7 +156,7 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("kind", list(range(B.W8A8_TILE_OVERRIDE_PANEL + 1)))
 def test_every_tile_shape_gives_identical_bits(kind):
     M, N, K = 300, 520, 704
     say(f"tile kind {kind}")

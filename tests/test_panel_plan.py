@@ -167,7 +167,7 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 1
-    for kind in range(7):
+    for kind in range(B.W8A8_TILE_OVERRIDE_PANEL):
         B.set_tile_override(kind)
         try:
             assert B.w8a8_gemm_plan(256, 34816, 5120, 1, 0)[0] == 1
