@@ -63,9 +63,12 @@ constexpr int NXCD = 8;        // XCDs on MI355X
 //   WGM x WGN   waves per workgroup        WTM x WTN  32x32 MFMA tiles per wave
 //   BK_         K bytes per LDS stage      NST_       LDS stages
 //   OCC_        workgroups per CU the register budget is sized for
-template <int WGM_, int WGN_, int WTM_, int WTN_, int BK_, int NST_, int OCC_, bool DIRECT_EPI_ = false>
+//   PREFETCH_   touch the L2 lines of a later stage (256-row tiles, NST = 2)
+template <int WGM_, int WGN_, int WTM_, int WTN_, int BK_, int NST_, int OCC_, bool DIRECT_EPI_ = false,
+          bool PREFETCH_ = false>
 struct Cfg {
     static constexpr bool DIRECT_EPI = DIRECT_EPI_;
+    static constexpr bool PREFETCH = PREFETCH_;
     static constexpr int WGM = WGM_, WGN = WGN_, WTM = WTM_, WTN = WTN_;
     static constexpr int NW = WGM * WGN;
     static constexpr int THREADS = 64 * NW;
@@ -92,7 +95,10 @@ struct Cfg {
                   "fills must cover the tile");
     static_assert(NST >= 2 && NST <= 4, "pipeline depth");
     static_assert(DIRECT_EPI || THREADS % (BN / 4) == 0, "epilogue sweep");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
+    static constexpr int PF_BYTES = PREFETCH ? 512 : 0;  // landing area of the L2 touches
+    static_assert(LDS_BYTES + PF_BYTES <= 160 * 1024, "LDS per workgroup");
+    static_assert(!PREFETCH || (NST == 2 && BM == 256 && BN % 8 == 0 && BN / 8 <= 64),
+                  "prefetch layout");
 };
 
 typedef __attribute__((address_space(3))) int8_t lds_i8;
@@ -104,6 +110,16 @@ typedef __attribute__((address_space(3))) int8_t lds_i8;
 // before the barrier that publishes the stage.
 __device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "memory");
+}
+
+// One wave instruction that touches one L2 line per lane: each lane copies 4
+// bytes from gbase + voff into LDS at lds + 4*lane, a landing area nobody
+// reads.  Its only purpose is to bring the line into the XCD's L2.
+__device__ __forceinline__ void l2_touch4(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(gbase), "s"(lds)
                  : "memory");
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     int tiles_m, int tiles_n, int group_m, int splitk, int kb_per_split,
     int32_t* __restrict__ partials) {
     constexpr int WTM = C::WTM, WTN = C::WTN, BK = C::BK, NST = C::NST;
-    __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS_BYTES + C::PF_BYTES];
 
     // ---- block -> (tile, split), XCD-contiguous and grouped along M
     const int nblocks = gridDim.x;
@@ -369,6 +385,42 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 if (more) load_frag(f0, la_n, lb_n, 0, q);
         }
     } else {
+        // ---- L2 prefetch (PREFETCH configurations).  The copies of a stage
+        // mostly miss in L2: the workgroups of an XCD run in step, so the
+        // ones sharing an operand panel request its lines together and all
+        // wait for the memory-side cache.  Here, PF_DIST stages ahead, wave 0
+        // touches one line per row of a quarter of the tile's activation rows
+        // (quarter tn % 4) and wave 1 of an eighth of its weight rows (eighth
+        // tm % 8).  Tiles are rastered 8 tile rows by consecutive tile
+        // columns per XCD, so the workgroups that share a panel split its
+        // rows between them instead of each touching all of them.  A touch
+        // is issued after the stage's copies, and waves 0 and 1 wait for all
+        // but their last vector-memory operation, so nothing waits on a
+        // touch until it is a stage old.  One line per row: with
+        // K % 128 == 64 half the rows' stage slices straddle two lines and
+        // only the first is touched.
+        constexpr int PF_DIST = 3;
+        const bool pf_wave = C::PREFETCH && wave < 2;
+        const int8_t* pf_base = a_tile;
+        uint32_t pf_off = 0;
+        lds_i8* const pf_lds = (lds_i8*)smem + C::LDS_BYTES + 256 * (wave & 1);
+        if (pf_wave) {
+            if (wave == 0) {
+                const int gr = min(row0 + (tn & 3) * (C::BM / 4) + lane % (C::BM / 4), M - 1);
+                pf_off = static_cast<uint32_t>(gr - row0) * static_cast<uint32_t>(K);
+            } else {
+                const int gc = min(col0 + (tm & 7) * (C::BN / 8) + lane % (C::BN / 8), N - 1);
+                pf_base = b_tile;
+                pf_off = static_cast<uint32_t>(gc - col0) * static_cast<uint32_t>(K);
+            }
+        }
+        auto prefetch = [&](int st) __attribute__((always_inline)) {
+            l2_touch4(pf_base + min(st, nst - 1) * BK, pf_off, pf_lds);
+        };
+        if (pf_wave && nst > 0) {
+#pragma unroll
+            for (int p = 1; p < PF_DIST; ++p) prefetch(p);
+        }
     #pragma unroll
         for (int p = 0; p < NST - 1; ++p)
             if (p < nst) issue(p, p);
@@ -382,7 +434,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 if (pending >= 1) wait_vm<C::LPS>();
                 else wait_vm<0>();
             } else {
-                wait_vm<0>();
+                // the touch of the previous stage may still be in flight
+                if (pf_wave && st > 0) wait_vm<1>();
+                else wait_vm<0>();
             }
             __syncthreads();
             // The copy of stage st + NST - 1 is issued unconditionally, with
@@ -428,6 +482,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 }
             }
             while (d < C::LPS) issue_one(fs, d++);
+            if (pf_wave) prefetch(st + PF_DIST);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -719,12 +774,12 @@ using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1>;  // 256x256, 4 waves, 128-byte stages x
 using Cfg1 = Cfg<2, 4, 4, 2, 64, 4, 1>;   // 256x256, 8 waves, 64-byte stages x4
 using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per CU
 using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU
-using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1>;  // 256x256, 8 waves, 128-byte stages x2
-using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true>;  // as 4, epilogue stored from the accumulators
+using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1, false, true>;  // 256x256, 8 waves, 128-byte stages x2
+using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true, true>;   // as 4, epilogue stored from the accumulators
 // 256x320, 8 waves of 64x160, 128-byte stages x2, epilogue from the
 // accumulators: N = 5120 is 16 such tiles, so M = 8192 makes 512 tiles, two
 // full rounds on 256 CUs where 256x256 tiles make 2.5
-using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, true>;
+using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, true, true>;
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {
