@@ -34,8 +34,8 @@ def _quant_case(M, K, seed, n_out=3, mult=30.0):
 
 # ------------------------------------------------------------------ quantisation
 
-# (1543, 5120) and (2357, 17408): more rows than workgroups resident at once,
-# so each workgroup takes several rows, with ragged remainders
+# (1543, 5120) and (2357, 17408): more rows than workgroups resident at once
+# (several rounds of workgroups), with ragged remainders
 @pytest.mark.parametrize("M,K", [(1, 64), (16, 256), (37, 1024), (300, 5120), (5, 17408), (2, 40960),
                                  (1543, 5120), (2357, 17408)])
 def test_quantize_matches_oracle(M, K):
