@@ -64,11 +64,14 @@ constexpr int NXCD = 8;        // XCDs on MI355X
 //   BK_         K bytes per LDS stage      NST_       LDS stages
 //   OCC_        workgroups per CU the register budget is sized for
 //   PREFETCH_   touch the L2 lines of a later stage (256-row tiles, NST = 2)
+//   EPI_H_      the LDS-staged epilogue parks the wave rows in EPI_H_ groups
+//               (one group per pass), so that a pass fits in the LDS
 template <int WGM_, int WGN_, int WTM_, int WTN_, int BK_, int NST_, int OCC_, bool DIRECT_EPI_ = false,
-          bool PREFETCH_ = false>
+          bool PREFETCH_ = false, int EPI_H_ = 1>
 struct Cfg {
     static constexpr bool DIRECT_EPI = DIRECT_EPI_;
     static constexpr bool PREFETCH = PREFETCH_;
+    static constexpr int EPI_H = EPI_H_;
     static constexpr int WGM = WGM_, WGN = WGN_, WTM = WTM_, WTN = WTN_;
     static constexpr int NW = WGM * WGN;
     static constexpr int THREADS = 64 * NW;
@@ -87,14 +90,15 @@ struct Cfg {
     static constexpr int LPS = A_LOADS + B_LOADS;     // fill instructions per wave per stage
     static constexpr int SUBSTEPS = BK / 32;          // MFMA K-steps per stage
     static constexpr int ACC_PER_WAVE = WTM * WTN * 16 * 64;  // int32 per wave
-    static constexpr int STAGED_ROWS = 32 * WGM;      // epilogue rows per pass
+    static_assert(WGM % EPI_H_ == 0, "wave-row groups");
+    static constexpr int STAGED_ROWS = 32 * WGM / EPI_H_;   // epilogue rows per pass
     static constexpr int LDR = BN + 4;                // staged row pitch (int32), 4 mod 64 banks
     static constexpr int EPI_BYTES = DIRECT_EPI ? 0 : STAGED_ROWS * LDR * 4 + (BM + BN) * 4;
     static constexpr int LDS_BYTES = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
     static_assert(A_LOADS * ROWS_PER_FILL * NW == BM && B_LOADS * ROWS_PER_FILL * NW == BN,
                   "fills must cover the tile");
     static_assert(NST >= 2 && NST <= 4, "pipeline depth");
-    static_assert(DIRECT_EPI || THREADS % (BN / 4) == 0, "epilogue sweep");
+    static_assert(DIRECT_EPI || (STAGED_ROWS * (BN / 4)) % THREADS == 0, "epilogue sweep");
     static constexpr int PF_BYTES = PREFETCH ? 512 : 0;  // landing area of the L2 touches
     static_assert(LDS_BYTES + PF_BYTES <= 160 * 1024, "LDS per workgroup");
     static_assert(!PREFETCH || (NST == 2 && BM == 256 && BN % 8 == 0 && BN / 8 <= 64),
@@ -555,14 +559,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             }
         }
     } else {
-        // ---- epilogue, in WTM passes of STAGED_ROWS rows.  Every wave parks one
-        // 32-row slice of its accumulators in LDS (row-major int32, four adjacent
-        // columns per 16-byte write; rows padded by 4 words so that the 16 lanes
-        // of one write phase, 16 different rows, hit 16 different bank groups).
-        // Then all threads sweep the slice in float4 chunks along rows, one
-        // 16-byte residual load and one 16-byte output store per chunk, fully
-        // coalesced.
+        // ---- epilogue, in WTM * EPI_H passes of STAGED_ROWS rows.  In pass
+        // (i, h) every wave of wave-row group h parks slice i (32 rows) of its
+        // accumulators in LDS (row-major int32, four adjacent columns per
+        // 16-byte write; rows padded by 4 words so that the 16 lanes of one
+        // write phase, 16 different rows, hit 16 different bank groups).  Then
+        // all threads sweep the parked rows in float4 chunks along rows (chunk
+        // c of the pass is parked row c / (BN/4), column chunk c % (BN/4)),
+        // one 16-byte residual load and one 16-byte output store per chunk,
+        // whole rows per wave instruction.
         constexpr int LDR = C::LDR;
+        constexpr int H = C::EPI_H;
+        constexpr int WRP = C::WGM / H;                    // wave rows parked per pass
         int32_t* stage = reinterpret_cast<int32_t*>(smem);
         float* s_sx = reinterpret_cast<float*>(smem + C::STAGED_ROWS * LDR * 4);
         float* s_sw = s_sx + C::BM;
@@ -578,83 +586,94 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                             (part || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                                       (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
         constexpr int C4 = C::BN / 4;                      // float4 chunks per staged row
-        constexpr int ROWS_PER_SWEEP = C::THREADS / C4;
-        constexpr int RPT = C::STAGED_ROWS / ROWS_PER_SWEEP;   // staged rows per thread
-        static_assert(C::STAGED_ROWS % ROWS_PER_SWEEP == 0, "epilogue sweep");
-        const int c4 = threadIdx.x % C4;
-        const int rsub = threadIdx.x / C4;
-        const int col = col0 + 4 * c4;
-        // Interior tile with aligned rows: a straight-line sweep, every LDS read
-        // issued before the first store.  Otherwise the checked loop below.
+        constexpr int CPT = C::STAGED_ROWS * C4 / C::THREADS;   // chunks per thread per pass
+        // chunks read from LDS before the first store of a batch (bounded so
+        // that the batch fits beside the accumulators still held)
+        constexpr int KB = CPT <= 8 ? CPT : (CPT % 2 == 0 ? 2 : 1);
+        static_assert(CPT % KB == 0, "sweep batches");
+        // staged row r of pass (i, h) is tile row (h * WRP + r / 32) * 32 * WTM + i * 32 + r % 32
+        auto tile_row = [](int r, int i, int h) { return (h * WRP + (r >> 5)) * 32 * WTM + i * 32 + (r & 31); };
+        // Interior tile with aligned rows: a straight-line sweep, the LDS reads
+        // of a batch issued before its first store.  Otherwise the checked
+        // loop below.
         const bool fast = vec_ok && row0 + C::BM <= M && col0 + C::BN <= N;
     #pragma unroll
-        for (int pass = 0; pass < WTM; ++pass) {
-            // accumulator slice i = pass of every wave -> staged rows wm*32 + r
-            const int lr = wm * 32 + (lane & 31);
+        for (int pass = 0; pass < WTM * H; ++pass) {
+            const int i = pass / H, h = pass % H;
+            if (wm / WRP == h) {
+                // accumulator slice i of this wave -> staged rows (wm % WRP) * 32 + r
+                const int lr = (wm % WRP) * 32 + (lane & 31);
     #pragma unroll
-            for (int j = 0; j < WTN; ++j) {
+                for (int j = 0; j < WTN; ++j) {
     #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int lc = wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                    *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) =
-                        i32x4{acc[pass][j][4 * g], acc[pass][j][4 * g + 1], acc[pass][j][4 * g + 2],
-                              acc[pass][j][4 * g + 3]};
+                    for (int g = 0; g < 4; ++g) {
+                        const int lc = wn * 32 * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                        *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) =
+                            i32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
+                    }
+                    sched_fence();
                 }
-                sched_fence();
             }
             __syncthreads();
-            const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
             if (fast) {
-                // staged row r = rsub + k * ROWS_PER_SWEEP is tile row
-                // (r / 32) * 32 * WTM + pass * 32 + r % 32
-                i32x4 av[RPT];
-                float sxv[RPT];
-                size_t ov[RPT];
     #pragma unroll
-                for (int k = 0; k < RPT; ++k) {
-                    const int r = rsub + k * ROWS_PER_SWEEP;
-                    const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
-                    av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
-                    sxv[k] = s_sx[lr];
-                    ov[k] = static_cast<size_t>(row0 + lr) * N + col;
-                }
-                if (part) {
+                for (int k0 = 0; k0 < CPT; k0 += KB) {
+                    i32x4 av[KB];
+                    float sxv[KB];
+                    float4 swv[KB];
+                    size_t ov[KB];
     #pragma unroll
-                    for (int k = 0; k < RPT; ++k) *reinterpret_cast<i32x4*>(part + ov[k]) = av[k];
-                } else if (residual) {
-                    float4 rv[RPT];
-    #pragma unroll
-                    for (int k = 0; k < RPT; ++k) rv[k] = *reinterpret_cast<const float4*>(residual + ov[k]);
-    #pragma unroll
-                    for (int k = 0; k < RPT; ++k) {
-                        float4 v;
-                        v.x = scale_acc_residual(av[k][0], sxv[k], sw4.x, rv[k].x);
-                        v.y = scale_acc_residual(av[k][1], sxv[k], sw4.y, rv[k].y);
-                        v.z = scale_acc_residual(av[k][2], sxv[k], sw4.z, rv[k].z);
-                        v.w = scale_acc_residual(av[k][3], sxv[k], sw4.w, rv[k].w);
-                        *reinterpret_cast<float4*>(y + ov[k]) = v;
+                    for (int k = 0; k < KB; ++k) {
+                        const int c = threadIdx.x + (k0 + k) * C::THREADS;
+                        const int r = c / C4, c4 = c % C4;
+                        const int lr = tile_row(r, i, h);
+                        av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
+                        sxv[k] = s_sx[lr];
+                        swv[k] = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
+                        ov[k] = static_cast<size_t>(row0 + lr) * N + col0 + 4 * c4;
                     }
-                } else {
+                    if (part) {
     #pragma unroll
-                    for (int k = 0; k < RPT; ++k) {
-                        float4 v;
-                        v.x = scale_acc(av[k][0], sxv[k], sw4.x);
-                        v.y = scale_acc(av[k][1], sxv[k], sw4.y);
-                        v.z = scale_acc(av[k][2], sxv[k], sw4.z);
-                        v.w = scale_acc(av[k][3], sxv[k], sw4.w);
-                        *reinterpret_cast<float4*>(y + ov[k]) = v;
+                        for (int k = 0; k < KB; ++k) *reinterpret_cast<i32x4*>(part + ov[k]) = av[k];
+                    } else if (residual) {
+                        float4 rv[KB];
+    #pragma unroll
+                        for (int k = 0; k < KB; ++k) rv[k] = *reinterpret_cast<const float4*>(residual + ov[k]);
+    #pragma unroll
+                        for (int k = 0; k < KB; ++k) {
+                            float4 v;
+                            v.x = scale_acc_residual(av[k][0], sxv[k], swv[k].x, rv[k].x);
+                            v.y = scale_acc_residual(av[k][1], sxv[k], swv[k].y, rv[k].y);
+                            v.z = scale_acc_residual(av[k][2], sxv[k], swv[k].z, rv[k].z);
+                            v.w = scale_acc_residual(av[k][3], sxv[k], swv[k].w, rv[k].w);
+                            *reinterpret_cast<float4*>(y + ov[k]) = v;
+                        }
+                    } else {
+    #pragma unroll
+                        for (int k = 0; k < KB; ++k) {
+                            float4 v;
+                            v.x = scale_acc(av[k][0], sxv[k], swv[k].x);
+                            v.y = scale_acc(av[k][1], sxv[k], swv[k].y);
+                            v.z = scale_acc(av[k][2], sxv[k], swv[k].z);
+                            v.w = scale_acc(av[k][3], sxv[k], swv[k].w);
+                            *reinterpret_cast<float4*>(y + ov[k]) = v;
+                        }
                     }
+                    sched_fence();
                 }
                 __syncthreads();
                 continue;
             }
-            for (int r = rsub; r < C::STAGED_ROWS; r += ROWS_PER_SWEEP) {
-                // staged row r is tile row (r / 32) * 32 * WTM + pass * 32 + r % 32
-                const int lr = (r >> 5) * 32 * WTM + pass * 32 + (r & 31);
+            for (int c = threadIdx.x; c < C::STAGED_ROWS * C4; c += C::THREADS) {
+                const int r = c / C4, c4 = c % C4;
+                const int lr = tile_row(r, i, h);
                 const int row = row0 + lr;
+                const int col = col0 + 4 * c4;
                 if (row >= M) continue;
                 const int4 a4 = *reinterpret_cast<const int4*>(stage + r * LDR + 4 * c4);
                 const float sxm = s_sx[lr];
+                const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
                 const size_t o = static_cast<size_t>(row) * N + col;
                 if (vec_ok && col + 3 < N) {
                     if (part) {
@@ -776,10 +795,11 @@ using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per 
 using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU
 using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1, false, true>;  // 256x256, 8 waves, 128-byte stages x2
 using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true, true>;   // as 4, epilogue stored from the accumulators
-// 256x320, 8 waves of 64x160, 128-byte stages x2, epilogue from the
-// accumulators: N = 5120 is 16 such tiles, so M = 8192 makes 512 tiles, two
-// full rounds on 256 CUs where 256x256 tiles make 2.5
-using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, true, true>;
+// 256x320, 8 waves of 64x160, 128-byte stages x2, LDS-staged epilogue in
+// two groups of wave rows (64 rows x 320 columns per pass): N = 5120 is 16
+// such tiles, so M = 8192 makes 512 tiles, two full rounds on 256 CUs where
+// 256x256 tiles make 2.5
+using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, false, true, 2>;
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {

@@ -47,7 +47,7 @@ struct GemmArgs {
 //   2: 256x128, 4 waves, 2 workgroups per CU        3: 128x128, 2 workgroups per CU
 //   4: 256x256, 8 waves, 128-byte K stages x2
 //   5: as 4, epilogue written straight from the accumulators
-//   6: 256x320, 8 waves, 128-byte K stages x2, epilogue from the accumulators
+//   6: 256x320, 8 waves, 128-byte K stages x2, LDS-staged epilogue in two passes of rows
 enum TileKind { TILE_KIND_0 = 0, TILE_KIND_1, TILE_KIND_2, TILE_KIND_3, TILE_KIND_4, TILE_KIND_5, TILE_KIND_6,
                 TILE_KINDS };
 

@@ -79,7 +79,7 @@ int w8a8_abi_version(void);
  * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
  * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
  * stages, 5: as 4 with the epilogue stored straight from the accumulators,
- * 6: 256x320 with 8 waves and the epilogue from the accumulators);
+ * 6: 256x320 with 8 waves);
  * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
  * hold the rows (by default it runs for 64 < M <= 512).  It never changes a
  * result bit, only speed.
