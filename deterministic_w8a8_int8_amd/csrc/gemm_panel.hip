@@ -434,7 +434,12 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
 struct PanelKind {
     int mw, nb, nset, nslot;
 };
-constexpr PanelKind kPanelKinds[] = {{1, 8, 3, 3}, {2, 8, 3, 3}, {2, 12, 3, 3}, {3, 8, 3, 3}, {4, 9, 3, 3}, {6, 9, 2, 2}};
+// Wide panels for wide layers (N in the tens of thousands); narrow ones for
+// N = 5120-like layers, where a wide kind would multiply columns past the
+// panel and every wave would read all of their weight fragments.
+constexpr PanelKind kPanelKinds[] = {{1, 8, 3, 3}, {2, 8, 3, 3}, {2, 12, 3, 3}, {3, 8, 3, 3}, {4, 9, 3, 3},
+                                     {6, 9, 2, 2}, {1, 4, 3, 3}, {2, 3, 3, 3}, {2, 4, 3, 3}, {2, 5, 3, 3},
+                                     {4, 5, 3, 3}};
 constexpr int kNumPanelKinds = sizeof(kPanelKinds) / sizeof(kPanelKinds[0]);
 
 constexpr int NCU = 256;
@@ -564,6 +569,11 @@ hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, 
         case 3: e = launch_panel_t<3, 8, 3, 3>(a, p, partials, stream); break;
         case 4: e = launch_panel_t<4, 9, 3, 3>(a, p, partials, stream); break;
         case 5: e = launch_panel_t<6, 9, 2, 2>(a, p, partials, stream); break;
+        case 6: e = launch_panel_t<1, 4, 3, 3>(a, p, partials, stream); break;
+        case 7: e = launch_panel_t<2, 3, 3, 3>(a, p, partials, stream); break;
+        case 8: e = launch_panel_t<2, 4, 3, 3>(a, p, partials, stream); break;
+        case 9: e = launch_panel_t<2, 5, 3, 3>(a, p, partials, stream); break;
+        case 10: e = launch_panel_t<4, 5, 3, 3>(a, p, partials, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || p.S <= 1 || a.acc_out) return e;

@@ -74,7 +74,7 @@ const char* w8a8_status_string(int status);
 int w8a8_abi_version(void);
 
 /* Tuning and test hook (host, process-wide): force the tile configuration of
- * the tiled GEMM for later calls.  -1 = automatic (the default); 0..5 pick
+ * the tiled GEMM for later calls.  -1 = automatic (the default); 0..6 pick
  * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
  * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
  * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
