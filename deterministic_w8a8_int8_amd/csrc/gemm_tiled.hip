@@ -49,6 +49,7 @@
 //     fl(fl(fl(float(acc))*sx)*sw) (+ r), rounding once per step, with no
 //     fused multiply-add (the whole file is built with -ffp-contract=off).
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -66,12 +67,16 @@ constexpr int NXCD = 8;        // XCDs on MI355X
 //   PREFETCH_   touch the L2 lines of a later stage (256-row tiles, NST = 2)
 //   EPI_H_      the LDS-staged epilogue parks the wave rows in EPI_H_ groups
 //               (one group per pass), so that a pass fits in the LDS
+//   MF16_       v_mfma_i32_16x16x64_i8 instead of v_mfma_i32_32x32x32_i8
+//               (NST = 2, BK = 128, LDS-staged epilogue)
 template <int WGM_, int WGN_, int WTM_, int WTN_, int BK_, int NST_, int OCC_, bool DIRECT_EPI_ = false,
-          bool PREFETCH_ = false, int EPI_H_ = 1>
+          bool PREFETCH_ = false, int EPI_H_ = 1, bool MF16_ = false>
 struct Cfg {
     static constexpr bool DIRECT_EPI = DIRECT_EPI_;
     static constexpr bool PREFETCH = PREFETCH_;
     static constexpr int EPI_H = EPI_H_;
+    static constexpr bool MF16 = MF16_;
+    static_assert(!MF16_ || (NST_ == 2 && BK_ == 128 && !DIRECT_EPI_), "16x16x64 path");
     static constexpr int WGM = WGM_, WGN = WGN_, WTM = WTM_, WTN = WTN_;
     static constexpr int NW = WGM * WGN;
     static constexpr int THREADS = 64 * NW;
@@ -279,18 +284,53 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
 #pragma unroll
     for (int s = 0; s < C::SUBSTEPS; ++s) chunk_off[s] = ((2 * s + (lane >> 5)) ^ rsw) * 16;
 
-    i32x16 acc[WTM][WTN];
+    // Accumulators: WTM x WTN tiles of 32x32 (16 int32 per lane each), or
+    // with 16x16x64 MFMAs 2*WTM x 2*WTN tiles of 16x16 (4 int32 per lane).
+    constexpr int AM = C::MF16 ? 2 * WTM : WTM, AN = C::MF16 ? 2 * WTN : WTN;
+    using AccV = typename std::conditional<C::MF16, i32x4, i32x16>::type;
+    constexpr int AE = C::MF16 ? 4 : 16;
+    AccV acc[AM][AN];
 #pragma unroll
-    for (int i = 0; i < WTM; ++i)
+    for (int i = 0; i < AM; ++i)
 #pragma unroll
-        for (int j = 0; j < WTN; ++j)
+        for (int j = 0; j < AN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+            for (int e = 0; e < AE; ++e) acc[i][j][e] = 0;
 
     // Fragments of one 32-byte K sub-step: WTM activation and WTN weight
     // fragments, 16 bytes per lane each.
     struct Frags {
         i32x4 a[WTM], b[WTN];
+    };
+    // ---- 16x16x64 fragments (MF16).  Fragment q of 16 rows starting at row
+    // wm*32*WTM + 16*q (activations) or wn*32*WTN + 16*q (weights); in
+    // K-block u of the 128-byte stage, lane l reads row (l & 15), logical
+    // chunk 4u + (l >> 4).  The held set is the smaller of the two.
+    constexpr int MF_FA = 2 * WTM, MF_FB = 2 * WTN;
+    constexpr bool MF_HOLD_B = MF_FB <= MF_FA;
+    constexpr int MF_NH = MF_HOLD_B ? MF_FB : MF_FA;
+    constexpr int MF_NS = MF_HOLD_B ? MF_FA : MF_FB;
+    const int mf_sw = row_swz<C::CHUNKS>(lane & 15);
+    const int mf_c0 = (((lane >> 4)) ^ mf_sw) * 16, mf_c1 = ((4 + (lane >> 4)) ^ mf_sw) * 16;
+    const int mf_a = (wm * 32 * WTM + (lane & 15)) * BK, mf_b = (wn * 32 * WTN + (lane & 15)) * BK;
+    auto mf_frag = [&](const int8_t* la, const int8_t* lb, bool is_b, int q, int u) __attribute__((always_inline)) {
+        const int8_t* base = is_b ? lb + mf_b : la + mf_a;
+        return *reinterpret_cast<const i32x4*>(base + q * 16 * BK + (u ? mf_c1 : mf_c0));
+    };
+    auto mf_held = [&](const int8_t* la, const int8_t* lb, int q, int u) __attribute__((always_inline)) {
+        return mf_frag(la, lb, MF_HOLD_B, q, u);
+    };
+    auto mf_strm = [&](const int8_t* la, const int8_t* lb, int q, int u) __attribute__((always_inline)) {
+        return mf_frag(la, lb, !MF_HOLD_B, q, u);
+    };
+    // product (streamed o, held k); the weight fragment is the first operand,
+    // so lane l's four results are four adjacent columns of row l & 15
+    auto mf_mma = [&](int o, int k, const i32x4& sv, const i32x4& hv) __attribute__((always_inline)) {
+        if constexpr (C::MF16) {
+            if constexpr (MF_HOLD_B) acc[o][k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hv, sv, acc[o][k], 0, 0, 0);
+            else acc[k][o] = __builtin_amdgcn_mfma_i32_16x16x64_i8(sv, hv, acc[k][o], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     auto load_frag = [&](Frags& f, const int8_t* la, const int8_t* lb, int s, int q) {
         if (q < WTM)
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     // fragment and, during the first sub-steps, one fill instruction of the
     // next stage.  Those issue in the shadow of the running MFMA instead of
     // stalling the matrix core in a block of their own.
-    if constexpr (NST >= 3) {
+    if constexpr (NST >= 3 && !C::MF16) {
         // Publish-ahead pipeline (64-byte stages).  The barrier of iteration
         // st publishes stage st+1 and frees the buffer of stage st-1, into
         // which stage st + NST - 1 is copied.  The first fragments of each
@@ -451,11 +491,51 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             const FillStage fs = fill_stage(min(st + NST - 1, nst - 1), (st + NST - 1) % NST);
             const int8_t* la = smem + (st % NST) * C::STAGE;
             const int8_t* lb = la + C::A_BYTES;
+            int d = 0;   // fill instructions issued so far in this stage
+            if constexpr (C::MF16) {
+                // ---- 16x16x64 MFMAs.  A 64-byte K-block of the stage takes
+                // 2*WTM x 2*WTN products.  The smaller fragment set (held) is
+                // read at the start of the K-block (the second K-block's
+                // during the first); the larger (streamed) passes through a
+                // ring of three, read two products-groups ahead.  Product
+                // group o multiplies streamed fragment o by every held one.
+                const int nkb_st = (half_last && st == nst - 1) ? 1 : 2;
+                i32x4 h[2][MF_NH];
+                i32x4 sr[3];
+    #pragma unroll
+                for (int q = 0; q < MF_NH; ++q) h[0][q] = mf_held(la, lb, q, 0);
+                sr[0] = mf_strm(la, lb, 0, 0);
+                sr[1] = mf_strm(la, lb, 1 % MF_NS, 1 / MF_NS);
+    #pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (u >= nkb_st) break;
+                    if ((u == 0) == (wave >= C::NW / 2)) __builtin_amdgcn_s_setprio(1);
+                    else __builtin_amdgcn_s_setprio(0);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int o = 0; o < MF_NS; ++o) {
+                        const int g = u * MF_NS + o;   // running index over the stage
+                        const i32x4 cur = sr[g % 3];
+                        // streamed fragment g + 2 (possibly of K-block 1)
+                        if (g + 2 < 2 * MF_NS && (g + 2) / MF_NS < nkb_st)
+                            sr[(g + 2) % 3] = mf_strm(la, lb, (g + 2) % MF_NS, (g + 2) / MF_NS);
+                        // the held set of K-block 1, halfway through K-block 0
+                        if (u == 0 && o == MF_NS / 2 && nkb_st > 1) {
+    #pragma unroll
+                            for (int q = 0; q < MF_NH; ++q) h[1][q] = mf_held(la, lb, q, 1);
+                        }
+    #pragma unroll
+                        for (int k = 0; k < MF_NH; ++k) {
+                            mf_mma(o, k, cur, h[u][k]);
+                            if (d < C::LPS) issue_one(fs, d++);
+                        }
+                    }
+                }
+            } else {
             const int nsub = (half_last && st == nst - 1) ? 2 : C::SUBSTEPS;
             Frags f[2];
     #pragma unroll
             for (int q = 0; q < WTM + WTN; ++q) load_frag(f[0], la, lb, 0, q);
-            int d = 0;   // fill instructions issued so far in this stage
     #pragma unroll
             for (int s = 0; s < C::SUBSTEPS; ++s) {
                 if (s >= nsub) break;
@@ -485,6 +565,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     while (q < WTM + WTN) load_frag(nxt, la, lb, s + 1, q++);
                 }
             }
+            }   // 32x32x32 stage body
             while (d < C::LPS) issue_one(fs, d++);
             if (pf_wave) prefetch(st + PF_DIST);
         }
@@ -601,6 +682,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
         for (int pass = 0; pass < WTM * H; ++pass) {
             const int i = pass / H, h = pass % H;
             if (wm / WRP == h) {
+                if constexpr (C::MF16) {
+                    // 16-row tiles 2i and 2i+1 of this wave -> staged rows
+                    // (wm % WRP) * 32 + 16 * hh + (lane & 15)
+    #pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int lr = (wm % WRP) * 32 + 16 * hh + (lane & 15);
+    #pragma unroll
+                        for (int j = 0; j < 2 * WTN; ++j) {
+                            const int lc = wn * 32 * WTN + j * 16 + 4 * (lane >> 4);
+                            *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) = acc[2 * i + hh][j];
+                        }
+                        sched_fence();
+                    }
+                } else {
                 // accumulator slice i of this wave -> staged rows (wm % WRP) * 32 + r
                 const int lr = (wm % WRP) * 32 + (lane & 31);
     #pragma unroll
@@ -613,6 +708,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                                   acc[i][j][4 * g + 3]};
                     }
                     sched_fence();
+                }
                 }
             }
             __syncthreads();
@@ -793,13 +889,13 @@ using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1>;  // 256x256, 4 waves, 128-byte stages x
 using Cfg1 = Cfg<2, 4, 4, 2, 64, 4, 1>;   // 256x256, 8 waves, 64-byte stages x4
 using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per CU
 using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU
-using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1, false, true>;  // 256x256, 8 waves, 128-byte stages x2
+using Cfg4 = Cfg<2, 4, 4, 2, 128, 2, 1, false, true, 1, true>;  // 256x256, 8 waves, 128-byte stages x2
 using Cfg5 = Cfg<2, 4, 4, 2, 128, 2, 1, true, true>;   // as 4, epilogue stored from the accumulators
 // 256x320, 8 waves of 64x160, 128-byte stages x2, LDS-staged epilogue in
 // two groups of wave rows (64 rows x 320 columns per pass): N = 5120 is 16
 // such tiles, so M = 8192 makes 512 tiles, two full rounds on 256 CUs where
 // 256x256 tiles make 2.5
-using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, false, true, 2>;
+using Cfg6 = Cfg<4, 2, 2, 5, 128, 2, 1, false, true, 2, true>;
 
 template <class C>
 hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hipStream_t stream) {
