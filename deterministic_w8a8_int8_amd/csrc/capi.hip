@@ -135,7 +135,7 @@ int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* 
 
 int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
                             int64_t* ops, void* stream) {
-    if ((operand_kind != 0 && operand_kind != 1) || blocks <= 0 || blocks > kMaxDim || iters <= 0 ||
+    if (operand_kind < 0 || operand_kind > 3 || blocks <= 0 || blocks > kMaxDim || iters <= 0 ||
         !sink || !aligned(sink, 4))
         return W8A8_ERR_INVALID_ARG;
     if (ops) *ops = w8a8::mfma_ceiling_ops(blocks, iters);

@@ -16,6 +16,9 @@
 //   0  A and B uniform on [-128, 127]
 //   1  A shaped like per-token-quantised activations (mostly 0 and +-1, a few
 //      large outlier values), B uniform
+//   2, 3  as 0 and 1, with each 32x32x32 product replaced by two
+//      v_mfma_i32_16x16x64_i8 on the same operand registers (the same number
+//      of operations, 16x16 accumulators)
 // The operands come from an integer hash of the thread and slot numbers.
 #include <algorithm>
 
@@ -30,6 +33,13 @@ constexpr int CEIL_THREADS = 512;
 
 __device__ __forceinline__ void mfma_acc(i32x16& c, const i32x4& a, const i32x4& b) {
     asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Two 16x16x64 products on two 16x16 accumulators: the operations of one
+// 32x32x32 product.
+__device__ __forceinline__ void mfma_acc16(i32x4& c0, i32x4& c1, const i32x4& a, const i32x4& b) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c0) : "v"(a), "v"(b));
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c1) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {
@@ -47,7 +57,7 @@ __device__ __forceinline__ int activation_like_byte(uint32_t h) {
     return ((h >> 20) & 1u) ? -v : v;
 }
 
-template <int KIND>
+template <int KIND, bool MF16>
 __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sink, int64_t iters) {
     const uint32_t t = threadIdx.x + blockIdx.x * CEIL_THREADS;
     i32x4 a[4][4], b[4][2];
@@ -66,23 +76,44 @@ __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sin
         for (int j = 0; j < 2; ++j)
             for (int e = 0; e < 4; ++e) b[s][j][e] = static_cast<int32_t>(mix32(t * 4096u + 2048u + s * 64u + j * 8u + e));
     }
-    i32x16 c[4][2];
-    for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 2; ++j)
-            for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
-    for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) mfma_acc(c[i][j], a[s][i], b[s][j]);
-    }
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     int32_t x = 0;
-    for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 2; ++j)
-            for (int e = 0; e < 16; ++e) x ^= c[i][j][e];
+    if constexpr (MF16) {
+        i32x4 c[4][2][2];
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j)
+                for (int h = 0; h < 2; ++h)
+                    for (int e = 0; e < 4; ++e) c[i][j][h][e] = 0;
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) mfma_acc16(c[i][j][0], c[i][j][1], a[s][i], b[s][j]);
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j)
+                for (int h = 0; h < 2; ++h)
+                    for (int e = 0; e < 4; ++e) x ^= c[i][j][h][e];
+    } else {
+        i32x16 c[4][2];
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j)
+                for (int e = 0; e < 16; ++e) c[i][j][e] = 0;
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) mfma_acc(c[i][j], a[s][i], b[s][j]);
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j)
+                for (int e = 0; e < 16; ++e) x ^= c[i][j][e];
+    }
     // keeps the products alive; the sink is written only for this one value
     if (x == 0x7a5c3e1f) sink[0] = x;
 }
@@ -126,12 +157,13 @@ int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters) {
 
 hipError_t launch_mfma_ceiling(int kind, int64_t blocks, int64_t iters, int32_t* sink,
                                hipStream_t stream) {
-    if (kind == 0)
-        hipLaunchKernelGGL(mfma_ceiling_kernel<0>, dim3(static_cast<unsigned>(blocks)),
-                           dim3(CEIL_THREADS), 0, stream, sink, iters);
-    else
-        hipLaunchKernelGGL(mfma_ceiling_kernel<1>, dim3(static_cast<unsigned>(blocks)),
-                           dim3(CEIL_THREADS), 0, stream, sink, iters);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(CEIL_THREADS);
+    switch (kind) {
+        case 0: hipLaunchKernelGGL((mfma_ceiling_kernel<0, false>), grid, block, 0, stream, sink, iters); break;
+        case 1: hipLaunchKernelGGL((mfma_ceiling_kernel<1, false>), grid, block, 0, stream, sink, iters); break;
+        case 2: hipLaunchKernelGGL((mfma_ceiling_kernel<0, true>), grid, block, 0, stream, sink, iters); break;
+        default: hipLaunchKernelGGL((mfma_ceiling_kernel<1, true>), grid, block, 0, stream, sink, iters); break;
+    }
     return hipGetLastError();
 }
 

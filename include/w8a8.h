@@ -104,11 +104,13 @@ int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, in
 
 /*
  * Diagnostic (not part of the layer): launch an MFMA-only kernel that runs
- * v_mfma_i32_32x32x32_i8 on register-resident operands, with no memory
- * traffic, so the caller can time the throughput the int8 matrix cores
- * sustain on a given kind of operand data.  operand_kind 0: A and B uniform
- * int8; 1: A shaped like per-token-quantised activations (mostly 0 and +-1),
- * B uniform.  blocks x 512 threads run `iters` iterations.  *ops (host,
+ * int8 MFMAs on register-resident operands, with no memory traffic, so the
+ * caller can time the throughput the int8 matrix cores sustain on a given
+ * kind of operand data.  operand_kind 0: v_mfma_i32_32x32x32_i8, A and B
+ * uniform int8; 1: the same with A shaped like per-token-quantised
+ * activations (mostly 0 and +-1), B uniform; 2 and 3: as 0 and 1 with
+ * v_mfma_i32_16x16x64_i8 (two per 32x32x32 product, the same operations).
+ * blocks x 512 threads run `iters` iterations.  *ops (host,
  * nullable) receives the number of int8 operations (2 per multiply-add)
  * launched.  sink: device int32, written only in the impossible case that
  * an xor of all accumulators equals a fixed constant (it keeps the work

@@ -134,7 +134,8 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_answer_head(p, 64, 8, p, 0, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_OK
     assert lib.w8a8_set_tile_override(99) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_set_tile_override(-2) == B.W8A8_ERR_INVALID_ARG
-    assert lib.w8a8_probe_mfma_ceiling(2, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_probe_mfma_ceiling(4, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_probe_mfma_ceiling(-1, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_mfma_ceiling(0, 0, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_stream_read(odd, 1024, p, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_stream_read(p, 1000, p, S) == B.W8A8_ERR_INVALID_ARG
