@@ -311,6 +311,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     constexpr int MF_NH = MF_HOLD_B ? MF_FB : MF_FA;
     constexpr int MF_NS = MF_HOLD_B ? MF_FA : MF_FB;
     constexpr int MF_FILL_EVERY = MF_NS * MF_NH / C::LPS > 1 ? MF_NS * MF_NH / C::LPS : 1;
+    // product group of K-block 0 that reads the first held fragment of K-block 1
+    constexpr int MF_H1_FIRST = MF_NS - MF_NH - 1 > 0 ? MF_NS - MF_NH - 1 : 0;
+    static_assert(MF_NS >= MF_NH && MF_H1_FIRST + MF_NH <= MF_NS, "held reads of K-block 1 inside K-block 0");
     const int mf_sw = row_swz<C::CHUNKS>(lane & 15);
     const int mf_c0 = (((lane >> 4)) ^ mf_sw) * 16, mf_c1 = ((4 + (lane >> 4)) ^ mf_sw) * 16;
     const int mf_a = (wm * 32 * WTM + (lane & 15)) * BK, mf_b = (wn * 32 * WTN + (lane & 15)) * BK;
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                 // 2*WTM x 2*WTN products.  The smaller fragment set (held) is
                 // read at the start of the K-block (the second K-block's
                 // during the first); the larger (streamed) passes through a
-                // ring of three, read two products-groups ahead.  Product
+                // ring of three, read two product groups ahead.  Product
                 // group o multiplies streamed fragment o by every held one.
                 // The copies of the next stage are spread evenly over the
                 // first K-block's products (issued in a burst, or spread over
@@ -520,17 +523,20 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     for (int o = 0; o < MF_NS; ++o) {
                         const int g = u * MF_NS + o;   // running index over the stage
                         const i32x4 cur = sr[g % 3];
-                        // streamed fragment g + 2 (possibly of K-block 1)
-                        if (g + 2 < 2 * MF_NS && (g + 2) / MF_NS < nkb_st)
-                            sr[(g + 2) % 3] = mf_strm(la, lb, (g + 2) % MF_NS, (g + 2) / MF_NS);
-                        // the held set of K-block 1, halfway through K-block 0
-                        if (u == 0 && o == MF_NS / 2 && nkb_st > 1) {
+                        // the held set of K-block 1, one fragment per product group
+                        // over the last groups of K-block 0
+                        if (u == 0 && nkb_st > 1) {
     #pragma unroll
-                            for (int q = 0; q < MF_NH; ++q) h[1][q] = mf_held(la, lb, q, 1);
+                            for (int q = 0; q < MF_NH; ++q)
+                                if (o == MF_H1_FIRST + q) h[1][q] = mf_held(la, lb, q, 1);
                         }
     #pragma unroll
                         for (int k = 0; k < MF_NH; ++k) {
                             mf_mma(o, k, cur, h[u][k]);
+                            // streamed fragment g + 2 (possibly of K-block 1), in the
+                            // shadow of the group's first product
+                            if (k == 0 && g + 2 < 2 * MF_NS && (g + 2) / MF_NS < nkb_st)
+                                sr[(g + 2) % 3] = mf_strm(la, lb, (g + 2) % MF_NS, (g + 2) / MF_NS);
                             if ((g * MF_NH + k) % MF_FILL_EVERY == 0 && d < C::LPS) issue_one(fs, d++);
                         }
                     }
