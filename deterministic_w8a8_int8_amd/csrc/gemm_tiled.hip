@@ -472,6 +472,86 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     #pragma unroll
         for (int p = 0; p < NST - 1; ++p)
             if (p < nst) issue(p, p);
+        if constexpr (C::MF16) {
+        // ---- 16x16x64 MFMAs.  A 64-byte K-block of the stage takes 2*WTM x
+        // 2*WTN products.  The smaller fragment set (held) is read at the start
+        // of the K-block (the second K-block's one fragment per product group
+        // during the first); the larger (streamed) passes through a ring of
+        // three, read two product groups ahead in the shadow of a product.
+        // Product group o multiplies streamed fragment o by every held one.
+        // The copies of the next stage are spread evenly over the first
+        // K-block's products (in a burst, or over the whole stage, they
+        // measured 6-10% slower).  The barrier that publishes the next stage
+        // comes two product groups before the end of the stage: by then every
+        // LDS read of the stage has been issued (the barrier waits for them),
+        // so the next stage's first fragments are read while the last two
+        // groups multiply, and the matrix pipe does not idle at the stage
+        // boundary.
+        i32x4 h[2][MF_NH];
+        i32x4 sr[3];
+        i32x4 nx[2];   // the next stage's first two streamed fragments
+        if (nst > 0) {
+            wait_vm<0>();
+            __syncthreads();
+    #pragma unroll
+            for (int q = 0; q < MF_NH; ++q) h[0][q] = mf_held(smem, smem + C::A_BYTES, q, 0);
+            sr[0] = mf_strm(smem, smem + C::A_BYTES, 0, 0);
+            sr[1] = mf_strm(smem, smem + C::A_BYTES, 1 % MF_NS, 1 / MF_NS);
+        }
+        for (int st = 0; st < nst; ++st) {
+            const bool more = st + 1 < nst;
+            const FillStage fs = fill_stage(min(st + 1, nst - 1), (st + 1) % 2);
+            const int8_t* la = smem + (st % 2) * C::STAGE;
+            const int8_t* lb = la + C::A_BYTES;
+            const int8_t* la_n = smem + ((st + 1) % 2) * C::STAGE;
+            const int8_t* lb_n = la_n + C::A_BYTES;
+            const int nkb_st = (half_last && st == nst - 1) ? 1 : 2;
+            if (st > 0) {
+                sr[0] = nx[0];
+                sr[1] = nx[1];
+            }
+            int d = 0;   // copies of the next stage issued so far
+    #pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (u >= nkb_st) break;
+                if ((u == 0) == (wave >= C::NW / 2)) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int o = 0; o < MF_NS; ++o) {
+                    const int g = u * MF_NS + o;   // running index over the stage
+                    if (u == nkb_st - 1 && o == MF_NS - 2) {
+                        // publish the next stage: its copies have landed (the
+                        // touch of the L2 prefetch may still be in flight)
+                        while (d < C::LPS) issue_one(fs, d++);
+                        if (pf_wave) prefetch(st + PF_DIST);
+                        if (pf_wave) wait_vm<1>();
+                        else wait_vm<0>();
+                        __syncthreads();
+                        if (more) {   // (never in a short last stage, whose products use h[0])
+    #pragma unroll
+                            for (int q = 0; q < MF_NH; ++q) h[0][q] = mf_held(la_n, lb_n, q, 0);
+                            nx[0] = mf_strm(la_n, lb_n, 0, 0);
+                            nx[1] = mf_strm(la_n, lb_n, 1 % MF_NS, 1 / MF_NS);
+                        }
+                    }
+                    const i32x4 cur = sr[g % 3];
+                    if (u == 0 && nkb_st > 1) {
+    #pragma unroll
+                        for (int q = 0; q < MF_NH; ++q)
+                            if (o == MF_H1_FIRST + q) h[1][q] = mf_held(la, lb, q, 1);
+                    }
+    #pragma unroll
+                    for (int k = 0; k < MF_NH; ++k) {
+                        mf_mma(o, k, cur, h[u][k]);
+                        if (k == 0 && g + 2 < 2 * MF_NS && (g + 2) / MF_NS < nkb_st)
+                            sr[(g + 2) % 3] = mf_strm(la, lb, (g + 2) % MF_NS, (g + 2) / MF_NS);
+                        if ((g * MF_NH + k) % MF_FILL_EVERY == 0 && d < C::LPS) issue_one(fs, d++);
+                    }
+                }
+            }
+        }
+        } else {
         for (int st = 0; st < nst; ++st) {
             const int pending = min(st + NST - 2, nst - 1) - st;   // stages issued after st
             if constexpr (NST >= 4) {
@@ -496,52 +576,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             const int8_t* la = smem + (st % NST) * C::STAGE;
             const int8_t* lb = la + C::A_BYTES;
             int d = 0;   // fill instructions issued so far in this stage
-            if constexpr (C::MF16) {
-                // ---- 16x16x64 MFMAs.  A 64-byte K-block of the stage takes
-                // 2*WTM x 2*WTN products.  The smaller fragment set (held) is
-                // read at the start of the K-block (the second K-block's
-                // during the first); the larger (streamed) passes through a
-                // ring of three, read two product groups ahead.  Product
-                // group o multiplies streamed fragment o by every held one.
-                // The copies of the next stage are spread evenly over the
-                // first K-block's products (issued in a burst, or spread over
-                // the whole stage, they measured 6-10% slower).
-                const int nkb_st = (half_last && st == nst - 1) ? 1 : 2;
-                i32x4 h[2][MF_NH];
-                i32x4 sr[3];
-    #pragma unroll
-                for (int q = 0; q < MF_NH; ++q) h[0][q] = mf_held(la, lb, q, 0);
-                sr[0] = mf_strm(la, lb, 0, 0);
-                sr[1] = mf_strm(la, lb, 1 % MF_NS, 1 / MF_NS);
-    #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    if (u >= nkb_st) break;
-                    if ((u == 0) == (wave >= C::NW / 2)) __builtin_amdgcn_s_setprio(1);
-                    else __builtin_amdgcn_s_setprio(0);
-                    __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-                    for (int o = 0; o < MF_NS; ++o) {
-                        const int g = u * MF_NS + o;   // running index over the stage
-                        const i32x4 cur = sr[g % 3];
-                        // the held set of K-block 1, one fragment per product group
-                        // over the last groups of K-block 0
-                        if (u == 0 && nkb_st > 1) {
-    #pragma unroll
-                            for (int q = 0; q < MF_NH; ++q)
-                                if (o == MF_H1_FIRST + q) h[1][q] = mf_held(la, lb, q, 1);
-                        }
-    #pragma unroll
-                        for (int k = 0; k < MF_NH; ++k) {
-                            mf_mma(o, k, cur, h[u][k]);
-                            // streamed fragment g + 2 (possibly of K-block 1), in the
-                            // shadow of the group's first product
-                            if (k == 0 && g + 2 < 2 * MF_NS && (g + 2) / MF_NS < nkb_st)
-                                sr[(g + 2) % 3] = mf_strm(la, lb, (g + 2) % MF_NS, (g + 2) / MF_NS);
-                            if ((g * MF_NH + k) % MF_FILL_EVERY == 0 && d < C::LPS) issue_one(fs, d++);
-                        }
-                    }
-                }
-            } else {
+            {
             const int nsub = (half_last && st == nst - 1) ? 2 : C::SUBSTEPS;
             Frags f[2];
     #pragma unroll
@@ -579,6 +614,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             while (d < C::LPS) issue_one(fs, d++);
             if (pf_wave) prefetch(st + PF_DIST);
         }
+        }   // 32x32x32 loop
     }
     __builtin_amdgcn_s_setprio(0);
     mfma_drain();
