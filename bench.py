@@ -414,7 +414,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(gu_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gu_tops / PEAK_INT8_TOPS, 4),
                 "traffic": measured_traffic("gemm_gate_up_long_prefill", "gemm_tiled"),
-                "kernel": "gemm_tiled (256x256 tile)", "shape": [M, N1, K1]}
+                "kernel": "gemm_tiled ({}x{} tile)".format(*B.w8a8_gemm_plan(M, N1, K1, 1, 0)[2:4]),
+                "shape": [M, N1, K1]}
     dn_us = timer.mean_us("gemm_down")
     down = {"us": round(dn_us, 1), "tops": round(2.0 * M * N2 * K2 / (dn_us * 1e-6) / 1e12, 1),
             "splitk": S}

@@ -962,7 +962,9 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hip
 struct KindInfo {
     int bm, bn;
     int per_cu;     // workgroups resident per CU
-    double weight;  // relative per-CU throughput of the shape
+    double weight;  // relative per-CU throughput of the shape (measured: with
+                    // 16x16x64 MFMAs the 256x320 tile runs gate+up 8192x34816x5120
+                    // 4% faster than 256x256 despite 14 rounds of 1.25x work)
 };
 // Same order as TileKind and the Cfg list.
 const KindInfo kKinds[TILE_KINDS] = {
@@ -972,7 +974,7 @@ const KindInfo kKinds[TILE_KINDS] = {
     {Cfg3::BM, Cfg3::BN, Cfg3::OCC, 0.70},
     {Cfg4::BM, Cfg4::BN, Cfg4::OCC, 1.00},
     {Cfg5::BM, Cfg5::BN, Cfg5::OCC, 0.97},
-    {Cfg6::BM, Cfg6::BN, Cfg6::OCC, 0.97},
+    {Cfg6::BM, Cfg6::BN, Cfg6::OCC, 1.07},
 };
 
 int tile_override = -1;
