@@ -100,8 +100,13 @@ def _extreme_rows(K, seed):
     return [np.asarray(r, np.float32) for r in rows], [np.asarray(v, np.float32) for v in smooths]
 
 
-@pytest.mark.parametrize("K", [1024, 5120, 17408, 40960])
-def test_quantize_extreme_values_match_oracle(K):
+# tall=True repeats each case over 1100 rows: batches of more than 1024 rows
+# read the smoothing values from global memory on the exact paths, smaller
+# ones from a copy in LDS; both must give the oracle's bits
+@pytest.mark.parametrize("K,tall", [(1024, False), (5120, False), (17408, False), (40960, False),
+                                    (5120, True), (17408, True)])
+def test_quantize_extreme_values_match_oracle(K, tall):
+    say(f"quantize extremes K={K} tall={tall}")
     rows, smooths = _extreme_rows(K, seed=K)
     for i, (x, s) in enumerate(zip(rows, smooths)):
         # the row alone and with ordinary rows around it (same smoothing)
@@ -109,6 +114,8 @@ def test_quantize_extreme_values_match_oracle(K):
         typical = np.float64(np.median(np.abs(x.astype(np.float64) / s)))
         other = (np.clip(rng.standard_normal(K), -3, 3) * typical * s).astype(np.float32)
         block = np.stack([x, other, x])
+        if tall:
+            block = np.tile(block, (367, 1))[:1100]
         with np.errstate(all="ignore"):
             assert np.isfinite(block).all() and np.isfinite(block / s).all(), "inputs must be finite"
         xq, sx = B.w8a8_quantize_act(dev(block), dev(s))
@@ -239,6 +246,28 @@ def test_residual_in_place():
     rd = dev(r)
     B.w8a8_gemm_splitk(dev(xq), dev(sx), dev(w), dev(sw), 2, residual=rd, y=rd)
     assert_bits_equal(host(rd), want, "in place, split 2")
+
+
+# Interior tiles of the 256x256 and 256x320 configurations with a residual
+# copy it into LDS one pass ahead of its use; ragged tiles take the checked
+# sweep.  Both, separate and in place (y aliasing the residual).
+@pytest.mark.parametrize("kind", [4, 6])
+@pytest.mark.parametrize("M,N,K", [(600, 640, 320), (1030, 960, 576)])
+def test_tiled_residual_epilogue(kind, M, N, K):
+    say(f"tiled residual kind={kind} M={M} N={N} K={K}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + 7 * kind, residual=True)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    d = dev(xq), dev(sx), dev(w), dev(sw)
+    B.set_tile_override(kind)
+    try:
+        got = host(B.w8a8_gemm(*d, residual=dev(r)))
+        rd = dev(r)
+        B.w8a8_gemm(*d, residual=rd, y=rd)
+        got_in_place = host(rd)
+    finally:
+        B.set_tile_override(-1)
+    assert_bits_equal(got, want, f"kind {kind}")
+    assert_bits_equal(got_in_place, want, f"kind {kind} in place")
 
 
 def test_rows_identical_across_kernels_and_batches():
