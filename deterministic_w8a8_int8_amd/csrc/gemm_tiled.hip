@@ -158,6 +158,18 @@ __device__ __forceinline__ void mfma_drain() {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// Chunks per thread whose LDS reads are issued before the first store of a
+// sweep batch in the 16x16x64 configurations.
+#ifndef MF16_SWEEP_BATCH
+#define MF16_SWEEP_BATCH 8
+#endif
+
+constexpr int largest_divisor_upto(int n, int cap) {
+    int d = cap < n ? cap : n;
+    while (d > 1 && n % d != 0) --d;
+    return d;
+}
+
 // Keeps the scheduler from mixing the work of neighbouring output tiles,
 // which bounds register pressure in the epilogue.
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -716,34 +728,42 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
         constexpr int CPT = C::STAGED_ROWS * C4 / C::THREADS;   // chunks per thread per pass
         // chunks read from LDS before the first store of a batch (bounded so
         // that the batch fits beside the accumulators still held)
-        constexpr int KB = CPT <= 8 ? CPT : (CPT % 2 == 0 ? 2 : 1);
+        constexpr int KB = C::MF16 ? largest_divisor_upto(CPT, MF16_SWEEP_BATCH) : CPT <= 8 ? CPT : (CPT % 2 == 0 ? 2 : 1);
         static_assert(CPT % KB == 0, "sweep batches");
+        // 16x16x64 accumulators: in every pass each wave parks PT of its
+        // 16-row tiles (staged rows (wm * PT + q) * 16 + (lane & 15)), so every
+        // wave frees accumulator registers from the first pass on and the
+        // sweeps have room for larger batches.
+        constexpr int PT = C::MF16 ? C::STAGED_ROWS / (16 * C::WGM) : 1;
+        constexpr int NPASS = C::MF16 ? 2 * WTM / PT : WTM * H;
+        static_assert(!C::MF16 || (PT >= 1 && C::STAGED_ROWS == 16 * C::WGM * PT && (2 * WTM) % PT == 0),
+                      "16-row parking");
         // staged row r of pass (i, h) is tile row (h * WRP + r / 32) * 32 * WTM + i * 32 + r % 32
         auto tile_row = [](int r, int i, int h) { return (h * WRP + (r >> 5)) * 32 * WTM + i * 32 + (r & 31); };
         // Interior tile with aligned rows: a straight-line sweep, the LDS reads
         // of a batch issued before its first store.  Otherwise the checked
         // loop below.
         const bool fast = vec_ok && row0 + C::BM <= M && col0 + C::BN <= N;
+        // Pass (i, h) with wrp wave rows per pass: the waves of wave-row
+        // group h park accumulator slice i (32 rows of each wave).
+        auto park = [&](int i, int h, int wrp) __attribute__((always_inline)) {
+            if (wm / wrp != h) return;
+            if constexpr (C::MF16) {
+                // 16-row tiles 2i and 2i+1 of this wave -> staged rows
+                // (wm % wrp) * 32 + 16 * hh + (lane & 15)
     #pragma unroll
-        for (int pass = 0; pass < WTM * H; ++pass) {
-            const int i = pass / H, h = pass % H;
-            if (wm / WRP == h) {
-                if constexpr (C::MF16) {
-                    // 16-row tiles 2i and 2i+1 of this wave -> staged rows
-                    // (wm % WRP) * 32 + 16 * hh + (lane & 15)
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int lr = (wm % wrp) * 32 + 16 * hh + (lane & 15);
     #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int lr = (wm % WRP) * 32 + 16 * hh + (lane & 15);
-    #pragma unroll
-                        for (int j = 0; j < 2 * WTN; ++j) {
-                            const int lc = wn * 32 * WTN + j * 16 + 4 * (lane >> 4);
-                            *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) = acc[2 * i + hh][j];
-                        }
-                        sched_fence();
+                    for (int j = 0; j < 2 * WTN; ++j) {
+                        const int lc = wn * 32 * WTN + j * 16 + 4 * (lane >> 4);
+                        *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) = acc[2 * i + hh][j];
                     }
-                } else {
-                // accumulator slice i of this wave -> staged rows (wm % WRP) * 32 + r
-                const int lr = (wm % WRP) * 32 + (lane & 31);
+                    sched_fence();
+                }
+            } else {
+                // accumulator slice i of this wave -> staged rows (wm % wrp) * 32 + r
+                const int lr = (wm % wrp) * 32 + (lane & 31);
     #pragma unroll
                 for (int j = 0; j < WTN; ++j) {
     #pragma unroll
@@ -755,8 +775,106 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     }
                     sched_fence();
                 }
+            }
+        };
+
+        // ---- residual epilogue of an interior tile.  Here the sweep needs
+        // the residual, and a wave's vector-memory counter retires in order:
+        // a residual load issued after the wave's stores can only be waited
+        // for together with those stores, which made every batch of the
+        // sweep wait for the previous batch's writes to complete.  Instead
+        // the residual of the next pass is copied into LDS
+        // (global_load_lds_dwordx4, each lane the chunks it will use itself)
+        // before this pass's stores, so a pass waits only for the previous
+        // pass's stores, issued a whole pass earlier.  Passes are half as
+        // tall (RH = 2H groups of one wave row) so that the parking area, the
+        // scales and two residual buffers fit in the LDS.
+        constexpr int RH = 2 * H;
+        constexpr int RROWS = 32 * C::WGM / RH;                // staged rows per pass
+        constexpr int RCPT = RROWS * C4 / C::THREADS;          // chunks per thread per pass
+        constexpr int RES_BYTES = RROWS * C::BN * 4;           // one pass of residual
+        constexpr int RB0 = (RROWS * LDR * 4 + 511) / 512 * 512;
+        constexpr int RB1 = ((C::STAGED_ROWS * LDR + C::BM + C::BN) * 4 + 511) / 512 * 512;
+        constexpr bool RES_LDS = C::MF16 && C::WGM % RH == 0 && RROWS == 32 &&
+                                 RROWS * C4 % C::THREADS == 0 && RB0 + RES_BYTES <= C::STAGED_ROWS * LDR * 4 &&
+                                 RB1 + RES_BYTES <= C::LDS_BYTES;
+        if constexpr (RES_LDS) {
+            // (every lane offset below stays under 2^32 bytes from the tile's first row)
+            if (fast && residual && !part && static_cast<int64_t>(C::BM) * N * 4 < (int64_t(1) << 32)) {
+                const int8_t* res_tile = reinterpret_cast<const int8_t*>(residual + static_cast<size_t>(row0) * N);
+                auto res_fill = [&](int pass) __attribute__((always_inline)) {
+                    const int i = pass / RH, h = pass % RH;
+                    lds_i8* const buf = (lds_i8*)smem + ((pass & 1) ? RB1 : RB0);
+    #pragma unroll
+                    for (int k = 0; k < RCPT; ++k) {
+                        const int c = threadIdx.x + k * C::THREADS;
+                        const int r = c / C4, c4 = c % C4;
+                        const int lr = (h + (r >> 5)) * 32 * WTM + i * 32 + (r & 31);
+                        const uint32_t off = (static_cast<uint32_t>(lr) * static_cast<uint32_t>(N) +
+                                              static_cast<uint32_t>(col0 + 4 * c4)) * 4u;
+                        lds_fill16(res_tile, off, buf + (k * C::THREADS + 64 * wave) * 16);
+                    }
+                };
+                res_fill(0);
+    #pragma unroll
+                for (int pass = 0; pass < WTM * RH; ++pass) {
+                    const int i = pass / RH, h = pass % RH;
+                    park(i, h, 1);
+                    __syncthreads();
+                    // this pass's residual has landed (the previous pass's
+                    // RCPT stores may still be in flight)
+                    if (pass == 0) wait_vm<0>();
+                    else wait_vm<RCPT>();
+                    if (pass + 1 < WTM * RH) res_fill(pass + 1);
+                    const float* rbuf = reinterpret_cast<const float*>(smem + ((pass & 1) ? RB1 : RB0));
+    #pragma unroll
+                    for (int k = 0; k < RCPT; ++k) {
+                        const int c = threadIdx.x + k * C::THREADS;
+                        const int r = c / C4, c4 = c % C4;
+                        const int lr = (h + (r >> 5)) * 32 * WTM + i * 32 + (r & 31);
+                        const i32x4 a = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
+                        const float4 r4 = *reinterpret_cast<const float4*>(rbuf + 4 * c);
+                        const float sxm = s_sx[lr];
+                        const float4 sw4 = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
+                        float4 v;
+                        v.x = scale_acc_residual(a[0], sxm, sw4.x, r4.x);
+                        v.y = scale_acc_residual(a[1], sxm, sw4.y, r4.y);
+                        v.z = scale_acc_residual(a[2], sxm, sw4.z, r4.z);
+                        v.w = scale_acc_residual(a[3], sxm, sw4.w, r4.w);
+                        *reinterpret_cast<float4*>(y + static_cast<size_t>(row0 + lr) * N + col0 + 4 * c4) = v;
+                        sched_fence();
+                    }
+                    __syncthreads();
+                }
+                return;
+            }
+        }
+
+        auto park16 = [&](int pass) __attribute__((always_inline)) {
+            if constexpr (C::MF16) {
+    #pragma unroll
+                for (int q = 0; q < PT; ++q) {
+                    const int lr = (wm * PT + q) * 16 + (lane & 15);
+    #pragma unroll
+                    for (int j = 0; j < 2 * WTN; ++j) {
+                        const int lc = wn * 32 * WTN + j * 16 + 4 * (lane >> 4);
+                        *reinterpret_cast<i32x4*>(stage + lr * LDR + lc) = acc[pass * PT + q][j];
+                    }
+                    sched_fence();
                 }
             }
+        };
+        // tile row of staged row r in pass `pass`
+        auto trow = [&](int r, int pass) __attribute__((always_inline)) {
+            if constexpr (C::MF16)
+                return (r / (16 * PT)) * 32 * WTM + 16 * (pass * PT + (r / 16) % PT) + (r & 15);
+            else
+                return tile_row(r, pass / H, pass % H);
+        };
+    #pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+            if constexpr (C::MF16) park16(pass);
+            else park(pass / H, pass % H, WRP);
             __syncthreads();
             if (fast) {
     #pragma unroll
@@ -769,7 +887,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                     for (int k = 0; k < KB; ++k) {
                         const int c = threadIdx.x + (k0 + k) * C::THREADS;
                         const int r = c / C4, c4 = c % C4;
-                        const int lr = tile_row(r, i, h);
+                        const int lr = trow(r, pass);
                         av[k] = *reinterpret_cast<const i32x4*>(stage + r * LDR + 4 * c4);
                         sxv[k] = s_sx[lr];
                         swv[k] = *reinterpret_cast<const float4*>(s_sw + 4 * c4);
@@ -809,7 +927,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
             }
             for (int c = threadIdx.x; c < C::STAGED_ROWS * C4; c += C::THREADS) {
                 const int r = c / C4, c4 = c % C4;
-                const int lr = tile_row(r, i, h);
+                const int lr = trow(r, pass);
                 const int row = row0 + lr;
                 const int col = col0 + 4 * c4;
                 if (row >= M) continue;
