@@ -60,17 +60,17 @@ __device__ __forceinline__ int8_t quantize_exact(float x, float s, float scale) 
 }
 
 // Fast quantisation with the proof described above; falls back to the exact
-// divisions when the approximate quotient is near a rounding boundary
-// (s_get() reads the smoothing value only then).
-template <class SGet>
-__device__ __forceinline__ int8_t quantize_fast(float x, float r, SGet s_get, float scale, float inv) {
+// divisions when the approximate quotient is near a rounding boundary.
+__device__ __forceinline__ int8_t quantize_fast(float x, float r, const float4* s4, int j, int c,
+                                                float scale, float inv) {
     const float t = (x * r) * inv;
     const float d = fabsf((t - floorf(t)) - 0.5f);
     float q;
     if (d > 0x1p-12f) {
         q = rintf(t);
     } else {
-        q = rintf((x / s_get()) / scale);
+        const float s = reinterpret_cast<const float*>(s4)[4 * j + c];
+        q = rintf((x / s) / scale);
     }
     q = fminf(fmaxf(q, -127.0f), 127.0f);
     return static_cast<int8_t>(static_cast<int>(q));
@@ -119,34 +119,19 @@ __device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d
 // NV float4 per thread held in registers: K <= NV * 4 * T; ROWS rows per
 // workgroup of T threads.  GIVEN: the per-token maximum comes from amax_in
 // (a row-parallel layer's global maximum) instead of the row itself.
-// SLDS: the exact paths read the smoothing values from a copy in LDS (4*K
-// bytes of dynamic shared memory).  Each thread copies and later reads only
-// its own columns, so the copy needs no barrier.  A reload from global
-// memory would queue behind the row loads of every workgroup on the CU (the
-// vector memory path is in order) and hold up the row maximum, which nearly
-// every row needs for about one element per wave.
-template <int NV, int T, int ROWS, bool GIVEN, bool SLDS>
+template <int NV, int T, int ROWS, bool GIVEN>
 __global__ __launch_bounds__(T) void quantize_rows_reg(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
     float* __restrict__ sx, const float* __restrict__ amax_in) {
     constexpr int NW = T / 64;
     __shared__ float redf[2][NW];
-    extern __shared__ float4 s_lds[];
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
     const int K4 = static_cast<int>(K >> 2);
     const int t = threadIdx.x;
-    auto s_at = [&](int j) __attribute__((always_inline)) {
-        if constexpr (SLDS) return s_lds[j];
-        else return s4[j];
-    };
-    auto s_one = [&](int j, int c) __attribute__((always_inline)) {
-        if constexpr (SLDS) return reinterpret_cast<const float*>(s_lds)[4 * j + c];
-        else return smooth[4 * j + c];
-    };
 
     // per-column reciprocals of the smoothing values, shared by the block's
-    // rows (the smoothing values themselves are read again on the rare exact
+    // rows (the smoothing values themselves are reloaded on the rare exact
     // paths).  A thread holding a smoothing value outside [2^-120, 2^120]
     // takes the exact divisions for all of its elements.
     float4 rv[NV];
@@ -155,9 +140,6 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
     for (int i = 0; i < NV; ++i) {
         const int j = t + i * T;
         const float4 sv = j < K4 ? s4[j] : f4(1.0f);
-        if constexpr (SLDS) {
-            if (j < K4) s_lds[j] = sv;
-        }
         rv[i] = make_float4(fast_rcp(sv.x), fast_rcp(sv.y), fast_rcp(sv.z), fast_rcp(sv.w));
         const float lo = fminf(fminf(sv.x, sv.y), fminf(sv.z, sv.w));
         const float hi = fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w));
@@ -213,7 +195,7 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 #pragma unroll
                 for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
                 if (any) {
-                    const float4 sv = s_at(j);
+                    const float4 sv = s4[j];
                     const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
@@ -237,14 +219,14 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
             uint32_t packed = 0;
             if (scale != 0.0f) {
                 if (exact) {
-                    const float4 sv = s_at(j);
+                    const float4 sv = s4[j];
                     packed = pack4(quantize_exact(xv[i].x, sv.x, scale), quantize_exact(xv[i].y, sv.y, scale),
                                    quantize_exact(xv[i].z, sv.z, scale), quantize_exact(xv[i].w, sv.w, scale));
                 } else {
-                    packed = pack4(quantize_fast(xv[i].x, rv[i].x, [&] { return s_one(j, 0); }, scale, inv),
-                                   quantize_fast(xv[i].y, rv[i].y, [&] { return s_one(j, 1); }, scale, inv),
-                                   quantize_fast(xv[i].z, rv[i].z, [&] { return s_one(j, 2); }, scale, inv),
-                                   quantize_fast(xv[i].w, rv[i].w, [&] { return s_one(j, 3); }, scale, inv));
+                    packed = pack4(quantize_fast(xv[i].x, rv[i].x, s4, j, 0, scale, inv),
+                                   quantize_fast(xv[i].y, rv[i].y, s4, j, 1, scale, inv),
+                                   quantize_fast(xv[i].z, rv[i].z, s4, j, 2, scale, inv),
+                                   quantize_fast(xv[i].w, rv[i].w, s4, j, 3, scale, inv));
                 }
             }
             qr[j] = packed;
@@ -304,34 +286,19 @@ __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     }
 }
 
-// The LDS copy of the smoothing values pays off while few rows share a CU
-// (the row maximum is then on the critical path): 256 x 17408 took 11.6
-// instead of 14.0 us.  With many rows per CU the memory path is the limit
-// and the copy measured 4-5% slower (8192 x 17408: 169 against 163 us), so
-// it is used for M <= S_LDS_MAX_M and rows of at most 20480 columns (two
-// workgroups' copies fit in one CU's 160 KiB).
-constexpr int64_t S_LDS_MAX_BYTES = 80 * 1024;
-constexpr int64_t S_LDS_MAX_M = 1024;
-
-template <int NV, int T, bool GIVEN>
-hipError_t launch_reg_given(const QuantArgs& a, hipStream_t stream) {
-    // One row per workgroup: measured faster than sharing the reciprocals
-    // over several rows, because more workgroups keep more rows in flight.
-    const int64_t s_bytes = 4 * a.K;
-    const dim3 grid(static_cast<unsigned>(a.M)), block(T);
-    const float* amax = GIVEN ? a.amax : nullptr;
-    if (s_bytes <= S_LDS_MAX_BYTES && a.M <= S_LDS_MAX_M)
-        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, GIVEN, true>), grid, block, static_cast<unsigned>(s_bytes),
-                           stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx, amax);
-    else
-        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, GIVEN, false>), grid, block, 0, stream, a.x, a.ldx,
-                           a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx, amax);
-    return hipGetLastError();
-}
-
 template <int NV, int T>
 hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
-    return a.amax ? launch_reg_given<NV, T, true>(a, stream) : launch_reg_given<NV, T, false>(a, stream);
+    // One row per workgroup: measured faster than sharing the reciprocals
+    // over several rows, because more workgroups keep more rows in flight.
+    if (a.amax)
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, true>), dim3(static_cast<unsigned>(a.M)), dim3(T),
+                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
+                           a.amax);
+    else
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, false>), dim3(static_cast<unsigned>(a.M)), dim3(T),
+                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
+                           nullptr);
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -100,9 +100,8 @@ def _extreme_rows(K, seed):
     return [np.asarray(r, np.float32) for r in rows], [np.asarray(v, np.float32) for v in smooths]
 
 
-# tall=True repeats each case over 1100 rows: batches of more than 1024 rows
-# read the smoothing values from global memory on the exact paths, smaller
-# ones from a copy in LDS; both must give the oracle's bits
+# tall=True repeats each case over 1100 rows, more workgroups than a round of
+# CUs holds, so the rare exact paths also run while other rows stream in
 @pytest.mark.parametrize("K,tall", [(1024, False), (5120, False), (17408, False), (40960, False),
                                     (5120, True), (17408, True)])
 def test_quantize_extreme_values_match_oracle(K, tall):
