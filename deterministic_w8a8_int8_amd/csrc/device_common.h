@@ -41,6 +41,23 @@ __device__ __forceinline__ float scale_acc_residual(int32_t acc, float sxm, floa
 // Quiet NaN for outputs whose inputs were rejected on the device.
 __device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
 
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+
+// One wave instruction: every lane copies 16 bytes from gbase + voff into LDS
+// at lds + 16*lane (global_load_lds_dwordx4; the LDS base goes through M0).
+// Issued as inline asm so that the compiler does not make later LDS reads of
+// other buffers wait for this copy; callers wait with an explicit vmcnt.
+__device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 // Wave64 maximum of a float through cross-lane shuffles (max is exact, so
 // the shuffle order cannot change the result).
 __device__ __forceinline__ float wave_max(float v) {

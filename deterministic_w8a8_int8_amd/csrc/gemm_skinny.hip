@@ -203,6 +203,144 @@ __global__ __launch_bounds__(KSPLIT > 1 ? 64 * KSPLIT : 256) void gemm_skinny(
     if (flagged && err_flag) atomicOr(err_flag, 1);
 }
 
+
+// ---- Weight stream through LDS (full products with at most 16 activation
+// rows staged in LDS, and enough column tiles to fill the GPU: the
+// full-vocabulary read-out).  Loads in the MFMA fragment layout touch 16 rows
+// x 64 bytes per wave instruction; a streaming probe over the lm_head's 1.27
+// GB read that pattern at 5.1 TB/s and whole 1 KiB-contiguous instructions at
+// 6.8 TB/s (with no LDS, many waves per CU).  Here the copy instructions
+// (global_load_lds_dwordx4) read RB = 64*KS contiguous bytes of 16/KS rows
+// each into LDS, and the fragments are read from LDS.  Each wave streams its
+// own 16 weight rows through its own NST-stage ring, so no barrier is
+// needed: a wave waits only for its own copies.  The ring bounds the bytes in
+// flight: 4 waves x 4 stages of 256-byte rows (two workgroups per CU) took
+// the 3 x 248000 x 5120 read-out from 216.7 to 211.9 us; 512- and 1024-byte
+// rows per stage, with fewer waves or stages, were slower (223-349 us).
+//   Stage t holds K-bytes [RB t, RB (t+1)) of the wave's 16 rows.  Copy
+// instruction j (0..KS-1) covers rows RPI*j .. RPI*j + RPI-1 (RPI = 16/KS):
+// lane l reads row r = RPI*j + l/CPR (CPR = 4*KS chunks of 16 bytes per row
+// and stage), chunk c = (l % CPR) ^ r, and lands at j*1024 + 16*l.  So chunk c
+// of row r sits at (r/RPI)*1024 + (r%RPI)*RB + 16*(c ^ r): a fragment read (16
+// rows at one chunk) hits 16 different 16-byte bank groups.
+#ifndef WL_WAVES_CFG
+#define WL_WAVES_CFG 4
+#define WL_NST_CFG 4
+#define WL_KSTEPS_CFG 4
+#endif
+constexpr int WL_KSTEPS = WL_KSTEPS_CFG;          // 64-byte K-steps per stage
+constexpr int WL_RB = 64 * WL_KSTEPS;             // bytes per row and stage
+constexpr int WL_CPR = WL_RB / 16;                // 16-byte chunks per row and stage
+constexpr int WL_RPI = 64 / WL_CPR;               // rows per copy instruction
+constexpr int WL_STAGE = 16 * WL_RB;              // bytes per wave-stage
+constexpr int WL_NST = WL_NST_CFG;                // stages per wave ring
+constexpr int WL_RING = WL_NST * WL_STAGE;        // bytes per wave
+constexpr int WL_WAVES = WL_WAVES_CFG;
+static_assert(WL_CPR >= 16 && WL_RPI * WL_CPR == 64 && WL_NST >= 2, "weight stream layout");
+static_assert((WL_NST - 2) * WL_KSTEPS <= 63, "copies in flight must fit the 6-bit vmcnt");
+
+// wait until the copies of stage t have landed, with `after` later stages
+// (KS instructions each) still allowed in flight
+template <int A>
+__device__ __forceinline__ void wl_wait(int after) {
+    if constexpr (A == 0) {
+        wait_vm<0>();
+    } else {
+        if (after >= A) wait_vm<A * WL_KSTEPS>();
+        else wl_wait<A - 1>(after);
+    }
+}
+
+__global__ __launch_bounds__(64 * WL_WAVES) void gemm_skinny_wlds(
+    const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
+    const float* __restrict__ sw, const float* residual, float* y, int64_t M, int64_t N, int64_t K,
+    int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: copy bases in SGPRs
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * WL_WAVES + wave) * 16;
+    extern __shared__ __attribute__((aligned(1024))) int8_t wl_lds[];
+    int8_t* const a_lds = wl_lds + WL_WAVES * WL_RING;
+    const int64_t apitch = K + 16;
+    const int kq = (lane >> 4) * 16;
+    {   // the activation rows, once per workgroup (as in the ALDS path)
+        const int64_t pieces = M * (K >> 4);
+        for (int64_t p = threadIdx.x; p < pieces; p += blockDim.x) {
+            const int64_t m = p / (K >> 4), c = p % (K >> 4);
+            *reinterpret_cast<i32x4*>(a_lds + m * apitch + c * 16) =
+                *reinterpret_cast<const i32x4*>(A + m * K + c * 16);
+        }
+        __syncthreads();
+    }
+    if (n0 >= N) return;
+    const bool arow_ok = (lane & 15) < M;
+    const int8_t* al = a_lds + (arow_ok ? (lane & 15) : 0) * apitch + kq;
+    auto a_frag = [&](int64_t s) -> i32x4 {
+        return arow_ok ? *reinterpret_cast<const i32x4*>(al + s * 64) : i32x4{0, 0, 0, 0};
+    };
+
+    // copy offsets of this lane (rows past N read row N-1; those columns are
+    // never stored)
+    uint32_t woff[WL_KSTEPS];
+#pragma unroll
+    for (int j = 0; j < WL_KSTEPS; ++j) {
+        const int r = WL_RPI * j + lane / WL_CPR;
+        const int64_t row = min(n0 + r, N - 1);
+        woff[j] = static_cast<uint32_t>((row - n0) * K) + static_cast<uint32_t>(16 * ((lane % WL_CPR) ^ r));
+    }
+    lds_i8* const ring = (lds_i8*)wl_lds + wave * WL_RING;
+    const int8_t* const wbase = W + n0 * K;
+    const int64_t nstages = K / WL_RB;
+    auto issue = [&](int64_t t) __attribute__((always_inline)) {
+        lds_i8* const dst = ring + (t % WL_NST) * WL_STAGE;
+        const int8_t* const src = wbase + t * WL_RB;
+#pragma unroll
+        for (int j = 0; j < WL_KSTEPS; ++j) lds_fill16(src, woff[j], dst + j * 1024);
+    };
+    // fragment of K-step s of a stage: row r = lane & 15, chunk 4s + lane/16
+    const int fr = lane & 15;
+    const int frow_off = (fr / WL_RPI) * 1024 + (fr % WL_RPI) * WL_RB;
+    const int8_t* const ring_g = wl_lds + wave * WL_RING;
+
+    i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < WL_NST - 1; ++t)
+        if (t < nstages) issue(t);
+    for (int64_t t = 0; t < nstages; ++t) {
+        wl_wait<WL_NST - 2>(static_cast<int>(min(static_cast<int64_t>(WL_NST - 2), nstages - 1 - t)));
+        // the buffer of stage t-1, multiplied in the last iteration: every
+        // LDS read of it has returned before the copy may overwrite it
+        if (t + WL_NST - 1 < nstages) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue(t + WL_NST - 1);
+        }
+        const int8_t* const st = ring_g + (t % WL_NST) * WL_STAGE + frow_off;
+#pragma unroll
+        for (int s = 0; s < WL_KSTEPS; ++s) {
+            const int c = 4 * s + (lane >> 4);
+            const i32x4 wv = *reinterpret_cast<const i32x4*>(st + 16 * (c ^ fr));
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_frag(t * WL_KSTEPS + s), wv, acc, 0, 0, 0);
+        }
+    }
+    // K-steps past the last whole stage, straight from memory
+    const int8_t* const wp = W + min(n0 + (lane & 15), N - 1) * K + kq;
+    for (int64_t s = nstages * WL_KSTEPS; s < (K >> 6); ++s) {
+        const i32x4 wv = *reinterpret_cast<const i32x4*>(wp + s * 64);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_frag(s), wv, acc, 0, 0, 0);
+    }
+
+    // epilogue: lane holds rows 4*(lane/16) + e of column n0 + lane%16
+    const int64_t col = n0 + (lane & 15);
+    if (col >= N) return;
+    const float swn = sw[col];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t m = 4 * (lane >> 4) + e;
+        if (m >= M) continue;
+        const int64_t o = m * ldy + col;
+        y[o] = residual ? scale_acc_residual(acc[e], sx[m], swn, residual[o]) : scale_acc(acc[e], sx[m], swn);
+    }
+}
+
 template <int R, int U, int KSPLIT, bool ALDS>
 hipError_t launch_r(const SkinnyArgs& a, hipStream_t stream) {
     const int64_t tiles = (a.N + 15) / 16;
@@ -236,6 +374,16 @@ hipError_t launch_rk(const SkinnyArgs& a, hipStream_t stream) {
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
+    const int64_t tiles = (a.N + 15) / 16;
+    const int64_t a_bytes = a.M * (a.K + 16);
+    if (a.M <= 16 && a_bytes <= kSkinnyLdsBytes && !a.gather && a.owner_c == 0 && tiles >= 1024 &&
+        a.K >= WL_RB && a.K * 16 < (int64_t(1) << 32)) {
+        const size_t lds = static_cast<size_t>(WL_WAVES * WL_RING + a_bytes);
+        hipLaunchKernelGGL(gemm_skinny_wlds, dim3(static_cast<unsigned>((tiles + WL_WAVES - 1) / WL_WAVES)),
+                           dim3(64 * WL_WAVES), lds, stream, a.xq, a.sx, a.w, a.sw, a.residual, a.y, a.M, a.N,
+                           a.K, a.ldy);
+        return hipGetLastError();
+    }
     if (a.M <= 16) {
         if (a.M * (a.K + 16) <= kSkinnyLdsBytes) return launch_rk<1, 8, true>(a, stream);
         return launch_rk<1, 8, false>(a, stream);

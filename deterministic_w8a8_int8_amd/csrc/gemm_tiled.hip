@@ -110,19 +110,6 @@ struct Cfg {
                   "prefetch layout");
 };
 
-typedef __attribute__((address_space(3))) int8_t lds_i8;
-
-// One wave instruction: every lane copies 16 bytes from gbase + voff into LDS
-// at lds + 16*lane (global_load_lds_dwordx4; the LDS base goes through M0).
-// Issued as inline asm so that the compiler does not make later LDS reads of
-// other buffers wait for this copy; the kernel waits with an explicit vmcnt
-// before the barrier that publishes the stage.
-__device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(gbase), "s"(lds)
-                 : "memory");
-}
 
 // One wave instruction that touches one L2 line per lane: each lane copies 4
 // bytes from gbase + voff into LDS at lds + 4*lane, a landing area nobody
@@ -136,9 +123,6 @@ __device__ __forceinline__ void l2_touch4(const int8_t* gbase, uint32_t voff, ld
 
 __device__ __forceinline__ void wait_fills() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until at most N of this wave's vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // One v_mfma_i32_32x32x32_i8 on a 32x32 int32 tile: c += w_frag * x_frag^T,
 // i.e. the weight rows index the tile's first dimension (see the layout note

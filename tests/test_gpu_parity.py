@@ -165,6 +165,19 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
+# At least 1024 column tiles and activation rows that fit in LDS: the weight
+# rows are copied into LDS in 256-byte K-stages (ragged N, K-steps past the
+# last whole stage, M from 1 to 16).
+@pytest.mark.parametrize("M,N,K", [(1, 16400, 256), (3, 16421, 320), (16, 20000, 640), (5, 17003, 1344)])
+@pytest.mark.parametrize("residual", [False, True])
+def test_skinny_weight_stream_through_lds(M, N, K, residual):
+    say(f"skinny lds stream M={M} N={N} K={K} residual={residual}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=5 * M + N + K, residual=residual)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+    assert_bits_equal(got, want, f"skinny {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("kind", list(range(B.W8A8_TILE_OVERRIDE_PANEL + 1)))
 def test_every_tile_shape_gives_identical_bits(kind):
     M, N, K = 300, 520, 704
