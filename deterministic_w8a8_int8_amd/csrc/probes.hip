@@ -118,24 +118,30 @@ __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sin
     if (x == 0x7a5c3e1f) sink[0] = x;
 }
 
-// Streaming read: every thread xors four independent 16-byte nontemporal
-// loads per iteration over a grid-stride loop, so the HBM read path is the
-// only limit.  The sink is written only if the xor equals a fixed constant.
+// Streaming read: workgroup b reads its own contiguous chunk of the buffer,
+// every wave instruction 1 KiB (64 lanes x 16 bytes, nontemporal), eight
+// independent loads in flight per thread, and xors them.  A grid-stride
+// pattern (consecutive instructions of a wave 8 MB apart) sustained 6.1-6.5
+// TB/s over 4 GiB; contiguous chunks 7.0-7.1 TB/s.  The sink is written only
+// if the xor equals a fixed constant.
 constexpr int READ_THREADS = 256;
+constexpr int READ_UNROLL = 8;
 
 __global__ __launch_bounds__(READ_THREADS) void stream_read_kernel(const i32x4* __restrict__ p,
-                                                                   int64_t n16, int32_t* sink) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * READ_THREADS;
-    int64_t i = static_cast<int64_t>(blockIdx.x) * READ_THREADS + threadIdx.x;
+                                                                   int64_t n16, int64_t chunk16,
+                                                                   int32_t* sink) {
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk16;
+    const int64_t b1 = b0 + chunk16 < n16 ? b0 + chunk16 : n16;
     i32x4 acc = {0, 0, 0, 0};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const i32x4 v0 = __builtin_nontemporal_load(p + i);
-        const i32x4 v1 = __builtin_nontemporal_load(p + i + stride);
-        const i32x4 v2 = __builtin_nontemporal_load(p + i + 2 * stride);
-        const i32x4 v3 = __builtin_nontemporal_load(p + i + 3 * stride);
-        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (READ_UNROLL - 1) * READ_THREADS < b1; i += READ_UNROLL * READ_THREADS) {
+        i32x4 v[READ_UNROLL];
+#pragma unroll
+        for (int u = 0; u < READ_UNROLL; ++u) v[u] = __builtin_nontemporal_load(p + i + u * READ_THREADS);
+#pragma unroll
+        for (int u = 0; u < READ_UNROLL; ++u) acc ^= v[u];
     }
-    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    for (; i < b1; i += READ_THREADS) acc ^= __builtin_nontemporal_load(p + i);
     const int32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
     if (x == 0x7a5c3e1f) sink[0] = x;
 }
@@ -144,9 +150,10 @@ __global__ __launch_bounds__(READ_THREADS) void stream_read_kernel(const i32x4* 
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream) {
     const int64_t n16 = bytes / 16;
-    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + READ_THREADS - 1) / READ_THREADS, 256 * 8));
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + READ_THREADS - 1) / READ_THREADS, 256 * 16));
+    const int64_t chunk16 = (n16 + blocks - 1) / blocks;
     hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(READ_THREADS), 0,
-                       stream, static_cast<const i32x4*>(buf), n16, sink);
+                       stream, static_cast<const i32x4*>(buf), n16, chunk16, sink);
     return hipGetLastError();
 }
 

@@ -121,9 +121,10 @@ int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int
 
 /*
  * Diagnostic (not part of the layer): read `bytes` of device memory at buf
- * once, with 16-byte nontemporal loads from a grid of 2048 x 256 threads,
- * so the caller can time the read bandwidth HBM sustains (use a buffer much
- * larger than the 256 MB last-level cache).  buf: device, 16-byte aligned,
+ * once, each of up to 4096 workgroups of 256 threads streaming its own
+ * contiguous chunk with 16-byte nontemporal loads (1 KiB per wave
+ * instruction), so the caller can time the read bandwidth HBM sustains (use
+ * a buffer much larger than the 256 MB last-level cache).  buf: device, 16-byte aligned,
  * bytes a positive multiple of 16.  sink: device int32, written only in the
  * impossible case that an xor of everything read equals a fixed constant.
  * Returns W8A8_ERR_INVALID_ARG for a bad argument.  Asynchronous on `stream`.
