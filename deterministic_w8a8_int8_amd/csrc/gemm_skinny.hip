@@ -223,19 +223,14 @@ __global__ __launch_bounds__(KSPLIT > 1 ? 64 * KSPLIT : 256) void gemm_skinny(
 // and stage), chunk c = (l % CPR) ^ r, and lands at j*1024 + 16*l.  So chunk c
 // of row r sits at (r/RPI)*1024 + (r%RPI)*RB + 16*(c ^ r): a fragment read (16
 // rows at one chunk) hits 16 different 16-byte bank groups.
-#ifndef WL_WAVES_CFG
-#define WL_WAVES_CFG 4
-#define WL_NST_CFG 4
-#define WL_KSTEPS_CFG 4
-#endif
-constexpr int WL_KSTEPS = WL_KSTEPS_CFG;          // 64-byte K-steps per stage
+constexpr int WL_KSTEPS = 4;                      // 64-byte K-steps per stage
 constexpr int WL_RB = 64 * WL_KSTEPS;             // bytes per row and stage
 constexpr int WL_CPR = WL_RB / 16;                // 16-byte chunks per row and stage
 constexpr int WL_RPI = 64 / WL_CPR;               // rows per copy instruction
 constexpr int WL_STAGE = 16 * WL_RB;              // bytes per wave-stage
-constexpr int WL_NST = WL_NST_CFG;                // stages per wave ring
+constexpr int WL_NST = 4;                         // stages per wave ring
 constexpr int WL_RING = WL_NST * WL_STAGE;        // bytes per wave
-constexpr int WL_WAVES = WL_WAVES_CFG;
+constexpr int WL_WAVES = 4;
 static_assert(WL_CPR >= 16 && WL_RPI * WL_CPR == 64 && WL_NST >= 2, "weight stream layout");
 static_assert((WL_NST - 2) * WL_KSTEPS <= 63, "copies in flight must fit the 6-bit vmcnt");
 

@@ -110,7 +110,6 @@ struct Cfg {
                   "prefetch layout");
 };
 
-
 // One wave instruction that touches one L2 line per lane: each lane copies 4
 // bytes from gbase + voff into LDS at lds + 4*lane, a landing area nobody
 // reads.  Its only purpose is to bring the line into the XCD's L2.
@@ -122,7 +121,6 @@ __device__ __forceinline__ void l2_touch4(const int8_t* gbase, uint32_t voff, ld
 }
 
 __device__ __forceinline__ void wait_fills() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 
 // One v_mfma_i32_32x32x32_i8 on a 32x32 int32 tile: c += w_frag * x_frag^T,
 // i.e. the weight rows index the tile's first dimension (see the layout note
@@ -143,10 +141,9 @@ __device__ __forceinline__ void mfma_drain() {
 }
 
 // Chunks per thread whose LDS reads are issued before the first store of a
-// sweep batch in the 16x16x64 configurations.
-#ifndef MF16_SWEEP_BATCH
-#define MF16_SWEEP_BATCH 8
-#endif
+// sweep batch in the 16x16x64 configurations (at most; the largest divisor of
+// the chunks per pass).
+constexpr int MF16_SWEEP_BATCH = 8;
 
 constexpr int largest_divisor_upto(int n, int cap) {
     int d = cap < n ? cap : n;
