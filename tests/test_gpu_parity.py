@@ -176,6 +176,10 @@ def test_skinny_weight_stream_through_lds(M, N, K, residual):
     want = oracle.gemm(xq, sx, w, sw, r)
     got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
     assert_bits_equal(got, want, f"skinny {M}x{N}x{K}")
+    if residual:   # the output may alias the residual
+        rd = dev(r)
+        B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=rd, y=rd)
+        assert_bits_equal(host(rd), want, f"skinny {M}x{N}x{K} in place")
 
 
 @pytest.mark.parametrize("kind", list(range(B.W8A8_TILE_OVERRIDE_PANEL + 1)))
