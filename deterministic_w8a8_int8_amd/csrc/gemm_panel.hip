@@ -65,10 +65,12 @@ struct PanelParams {
     int S, kb_per_split;        // K splits (64-byte K-blocks per split)
 };
 
-// Chunk swizzle of an LDS row: the 16 rows that one fragment read touches
-// (same logical chunk) land in 16 distinct 16-byte bank groups of 256 bytes
-// (64 banks), and any 8 consecutive rows in 8 distinct groups of 128 bytes.
-__device__ __forceinline__ int panel_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk swizzle of a 128-byte LDS row. A 128-bit LDS read is served 32
+// lanes at a time over a 512-byte window (four rows); the swizzle is constant
+// on row pairs and steps through 0..7 over rows 0..15, so the 32 lanes of a
+// fragment read (16 rows, two neighbouring logical chunks) hit 32 distinct
+// 16-byte bank groups, and each 16 of them 16 distinct groups of 256 bytes.
+__device__ __forceinline__ int panel_swz(int r) { return ((r >> 2) & 3) * 2 + ((r >> 1) & 1); }
 
 // Smallest divisor of g that is at least `want` (the fragment ring's size:
 // its phase must repeat every stage).

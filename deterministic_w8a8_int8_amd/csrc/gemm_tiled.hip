@@ -156,12 +156,14 @@ constexpr int largest_divisor_upto(int n, int cap) {
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 // Swizzle of the 16-byte chunk index inside an LDS row of CHUNKS chunks.
-// Rows r..r+15 read at one logical chunk land in 16 distinct 16-byte bank
-// groups of a 256-byte window (64 banks), and rows r..r+7 in 8 distinct
-// groups of a 128-byte window (32 banks).
+// For 128-byte rows a 128-bit LDS read is served 32 lanes at a time over a
+// 512-byte window (four rows): the swizzle is constant on row pairs and
+// steps through 0..7 over rows 0..15, so the 16 rows of a fragment read at
+// two neighbouring logical chunks hit 32 distinct 16-byte bank groups, and
+// any 16 of those lanes hit 16 distinct groups of a 256-byte window.
 template <int CHUNKS>
 __device__ __forceinline__ int row_swz(int r) {
-    if constexpr (CHUNKS == 8) return (r & 7) ^ ((r >> 3) & 1);
+    if constexpr (CHUNKS == 8) return ((r >> 2) & 3) * 2 + ((r >> 1) & 1);
     else return ((r >> 1) & 3) ^ (((r >> 3) & 1) * 3);
 }
 

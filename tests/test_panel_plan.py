@@ -33,7 +33,7 @@ def block_map(nblocks):
 
 
 def swz(r):
-    return (r & 7) ^ ((r >> 3) & 1)
+    return ((r >> 2) & 3) * 2 + ((r >> 1) & 1)
 
 
 def check_plan(M, N, K, plan):
@@ -124,6 +124,11 @@ def check_plan(M, N, K, plan):
                 b = ((lane[16 * ph:16 * ph + 16] & 15) * ROW_BYTES + f_off[16 * ph:16 * ph + 16] % ROW_BYTES)
                 groups = (b % 256) // 16
                 assert len(set(groups.tolist())) == 16
+            # served 32 lanes at a time over a 512-byte window: 32 distinct groups
+            for half in range(2):
+                sl = slice(32 * half, 32 * half + 32)
+                b = (lane[sl] & 15) * ROW_BYTES + f_off[sl] % ROW_BYTES
+                assert len(set(((b % 512) // 16).tolist())) == 32
     assert (kcover == 1).all(), "K splits must tile the K-blocks exactly once"
     assert (cover == 1).all(), "every (row block, column block) once per K split"
 
