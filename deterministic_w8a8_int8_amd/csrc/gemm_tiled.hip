@@ -442,7 +442,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
         // touch until it is a stage old.  One line per row: with
         // K % 128 == 64 half the rows' stage slices straddle two lines and
         // only the first is touched.
-        constexpr int PF_DIST = 3;
+        constexpr int PF_DIST = 2;
         const bool pf_wave = C::PREFETCH && wave < 2;
         const int8_t* pf_base = a_tile;
         uint32_t pf_off = 0;
