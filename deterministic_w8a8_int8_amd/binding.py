@@ -29,7 +29,8 @@ W8A8_MAX_CANDIDATES = 64
 W8A8_MAX_SPLITK = 64
 W8A8_TILE_OVERRIDE_PANEL = 7
 
-# Every symbol include/w8a8.h declares, with its ctypes signature.
+# Every symbol the headers in include/ declare (w8a8.h, w8a8_diag.h), with its
+# ctypes signature.
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "w8a8_status_string": (ctypes.c_char_p, [_I32]),
@@ -136,6 +137,35 @@ def _want(t, dtype, name):
         raise TypeError(f"{name} must be a GPU tensor")
 
 
+def _need(t, dtype, numel, name):
+    """A caller-supplied buffer: right dtype, on the GPU, contiguous and
+    exactly `numel` elements.  The C ABI receives bare pointers, so a short
+    buffer would otherwise be read or written past its end."""
+    _want(t, dtype, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    return t
+
+
+def _new(shape, dtype, device, stream):
+    """An output or workspace the caller did not pass, allocated on the
+    stream the call runs on, so that torch's caching allocator does not hand
+    the block to other work before that stream is done with it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _out(t, shape, dtype, device, stream, name):
+    n = 1
+    for d in shape:
+        n *= d
+    return _new(shape, dtype, device, stream) if t is None else _need(t, dtype, n, name)
+
+
 def w8a8_quantize_act(x, smooth, row_idx=None, xq=None, sx=None, stream=None):
     """Per-token int8 quantisation of x [rows, K] (row stride may exceed K).
     Returns (xq int8 [M,K], sx float32 [M]); M = len(row_idx) or rows."""
@@ -144,15 +174,14 @@ def w8a8_quantize_act(x, smooth, row_idx=None, xq=None, sx=None, stream=None):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, K = x.shape
+    _need(smooth, torch.float32, K, "smooth")
     if row_idx is not None:
-        _want(row_idx, torch.int32, "row_idx")
+        _need(row_idx, torch.int32, row_idx.numel(), "row_idx")
         M = row_idx.numel()
     else:
         M = rows
-    if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if sx is None:
-        sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    xq = _out(xq, (M, K), torch.int8, x.device, stream, "xq")
+    sx = _out(sx, (M,), torch.float32, x.device, stream, "sx")
     _check(_lib.w8a8_quantize_act(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth), M, K,
                                   _ptr(xq), _ptr(sx), _stream(stream)), "w8a8_quantize_act")
     return xq, sx
@@ -178,8 +207,7 @@ def _gemm_shapes(xq, sx, w, sw, residual):
 def w8a8_gemm(xq, sx, w, sw, residual=None, y=None, stream=None):
     """y = fixed epilogue of the exact int32 product xq @ w^T (+ residual)."""
     M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    y = _out(y, (M, N), torch.float32, xq.device, stream, "y")
     _check(_lib.w8a8_gemm(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y), M, N, K,
                           _stream(stream)), "w8a8_gemm")
     return y
@@ -192,19 +220,20 @@ def w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) -> int:
     return n
 
 
-def splitk_workspace(M, N, K, splitk, device="cuda"):
+def splitk_workspace(M, N, K, splitk, device="cuda", stream=None):
     """A workspace of the size w8a8_gemm_splitk needs (contents irrelevant)."""
     n = w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk)
-    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
+    return _new((max(n, 1),), torch.uint8, device, stream)
 
 
 def w8a8_gemm_splitk(xq, sx, w, sw, splitk, residual=None, y=None, workspace=None, stream=None):
     """Same result as w8a8_gemm, K split into `splitk` integer partials."""
     M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    y = _out(y, (M, N), torch.float32, xq.device, stream, "y")
     if workspace is None:
-        workspace = splitk_workspace(M, N, K, splitk, xq.device)
+        workspace = splitk_workspace(M, N, K, splitk, xq.device, stream)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     _check(_lib.w8a8_gemm_splitk(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y),
                                  M, N, K, int(splitk), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -225,11 +254,18 @@ def w8a8_readout_candidates(xq, sx, w_vocab, sw_vocab, cand, logits=None, err_fl
             raise ValueError(f"{n} must be contiguous")
     M, K = xq.shape
     V = w_vocab.shape[0]
-    C = cand.shape[1] if cand.dim() == 2 else 0
-    if cand.shape[0] != M:
+    if cand.dim() != 2 or cand.shape[0] != M:
         raise ValueError("cand must be [M, C]")
-    if logits is None:
-        logits = torch.empty((M, C), dtype=torch.float32, device=xq.device)
+    C = cand.shape[1]
+    if w_vocab.dim() != 2 or w_vocab.shape[1] != K:
+        raise ValueError("w_vocab must be [V, K]")
+    _need(sx, torch.float32, M, "sx")
+    _need(sw_vocab, torch.float32, V, "sw_vocab")
+    if err_flag is not None:
+        _want(err_flag, torch.int32, "err_flag")
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold at least one int32")
+    logits = _out(logits, (M, C), torch.float32, xq.device, stream, "logits")
     _check(_lib.w8a8_readout_candidates(_ptr(xq), _ptr(sx), M, K, _ptr(w_vocab), _ptr(sw_vocab), V,
                                         _ptr(cand), C, _ptr(logits), _ptr(err_flag), _stream(stream)),
            "w8a8_readout_candidates")
@@ -252,8 +288,9 @@ def w8a8_requantize_q8_0(q, d_bits, smooth, w=None, sw=None, stream=None):
     N, K = q.shape
     if d_bits.shape != (N, K // 32):
         raise ValueError("d_bits must be [N, K/32]")
-    w = torch.empty((N, K), dtype=torch.int8, device=q.device) if w is None else w
-    sw = torch.empty((N,), dtype=torch.float32, device=q.device) if sw is None else sw
+    _need(smooth, torch.float32, K, "smooth")
+    w = _out(w, (N, K), torch.int8, q.device, stream, "w")
+    sw = _out(sw, (N,), torch.float32, q.device, stream, "sw")
     _check(_lib.w8a8_requantize_q8_0(_ptr(q), _ptr(d_bits), _ptr(smooth), N, K, _ptr(w), _ptr(sw),
                                      _stream(stream)), "w8a8_requantize_q8_0")
     return w, sw
@@ -267,12 +304,13 @@ def w8a8_row_absmax(x, smooth, row_idx=None, amax=None, accumulate=False, stream
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, K = x.shape
+    _need(smooth, torch.float32, K, "smooth")
+    if row_idx is not None:
+        _need(row_idx, torch.int32, row_idx.numel(), "row_idx")
     M = row_idx.numel() if row_idx is not None else rows
-    if amax is None:
-        if accumulate:
-            raise ValueError("accumulate needs an existing amax")
-        amax = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _want(amax, torch.float32, "amax")
+    if amax is None and accumulate:
+        raise ValueError("accumulate needs an existing amax")
+    amax = _out(amax, (M,), torch.float32, x.device, stream, "amax")
     _check(_lib.w8a8_row_absmax(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth), M, K,
                                 1 if accumulate else 0, _ptr(amax), _stream(stream)), "w8a8_row_absmax")
     return amax
@@ -286,9 +324,13 @@ def w8a8_quantize_act_amax(x, smooth, amax, row_idx=None, xq=None, sx=None, stre
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, K = x.shape
+    _need(smooth, torch.float32, K, "smooth")
+    if row_idx is not None:
+        _need(row_idx, torch.int32, row_idx.numel(), "row_idx")
     M = row_idx.numel() if row_idx is not None else rows
-    xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
-    sx = torch.empty((M,), dtype=torch.float32, device=x.device) if sx is None else sx
+    _need(amax, torch.float32, M, "amax")
+    xq = _out(xq, (M, K), torch.int8, x.device, stream, "xq")
+    sx = _out(sx, (M,), torch.float32, x.device, stream, "sx")
     _check(_lib.w8a8_quantize_act_amax(_ptr(x), x.stride(0), rows, _ptr(row_idx), _ptr(smooth),
                                        _ptr(amax), M, K, _ptr(xq), _ptr(sx), _stream(stream)),
            "w8a8_quantize_act_amax")
@@ -305,8 +347,7 @@ def w8a8_gemm_int32(xq, w, acc=None, stream=None):
     N = w.shape[0]
     if w.shape[1] != K:
         raise ValueError("w must be [N, K]")
-    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if acc is None else acc
-    _want(acc, torch.int32, "acc")
+    acc = _out(acc, (M, N), torch.int32, xq.device, stream, "acc")
     _check(_lib.w8a8_gemm_int32(_ptr(xq), _ptr(w), M, N, K, _ptr(acc), _stream(stream)), "w8a8_gemm_int32")
     return acc
 
@@ -319,7 +360,11 @@ def w8a8_epilogue_int32(parts, sx, sw, residual=None, y=None, stream=None):
     if parts.dim() != 3 or not parts.is_contiguous():
         raise ValueError("parts must be a contiguous [S, M, N] tensor")
     S, M, N = parts.shape
-    y = torch.empty((M, N), dtype=torch.float32, device=parts.device) if y is None else y
+    _need(sx, torch.float32, M, "sx")
+    _need(sw, torch.float32, N, "sw")
+    if residual is not None:
+        _need(residual, torch.float32, M * N, "residual")
+    y = _out(y, (M, N), torch.float32, parts.device, stream, "y")
     _check(_lib.w8a8_epilogue_int32(_ptr(parts), S, _ptr(sx), _ptr(sw), _ptr(residual), _ptr(y), M, N,
                                     _stream(stream)), "w8a8_epilogue_int32")
     return y
@@ -331,9 +376,7 @@ def w8a8_candidate_softmax(logits, probs=None, stream=None):
     if logits.dim() != 2 or not logits.is_contiguous():
         raise ValueError("logits must be a contiguous [M, C] tensor")
     M, C = logits.shape
-    if probs is None:
-        probs = torch.empty((M, C), dtype=torch.float64, device=logits.device)
-    _want(probs, torch.float64, "probs")
+    probs = _out(probs, (M, C), torch.float64, logits.device, stream, "probs")
     _check(_lib.w8a8_candidate_softmax(_ptr(logits), M, C, _ptr(probs), _stream(stream)),
            "w8a8_candidate_softmax")
     return probs
@@ -353,14 +396,23 @@ def w8a8_answer_head(h, answer_rows, smooth, w_vocab, sw_vocab, cand, xq=None, s
         raise ValueError("h must be 2-D with unit column stride")
     rows, K = h.shape
     M = answer_rows.numel()
-    C = cand.shape[1] if cand.dim() == 2 else 0
-    if cand.shape[0] != M or not cand.is_contiguous() or not w_vocab.is_contiguous():
+    if cand.dim() != 2 or cand.shape[0] != M or not cand.is_contiguous() or not w_vocab.is_contiguous():
         raise ValueError("cand must be a contiguous [M, C] tensor and w_vocab contiguous")
+    C = cand.shape[1]
+    if w_vocab.dim() != 2 or w_vocab.shape[1] != K:
+        raise ValueError("w_vocab must be [V, K]")
+    _need(answer_rows, torch.int32, M, "answer_rows")
+    _need(smooth, torch.float32, K, "smooth")
+    _need(sw_vocab, torch.float32, w_vocab.shape[0], "sw_vocab")
+    if err_flag is not None:
+        _want(err_flag, torch.int32, "err_flag")
+        if err_flag.numel() < 1:
+            raise ValueError("err_flag must hold at least one int32")
     dev = h.device
-    xq = torch.empty((M, K), dtype=torch.int8, device=dev) if xq is None else xq
-    sx = torch.empty((M,), dtype=torch.float32, device=dev) if sx is None else sx
-    logits = torch.empty((M, C), dtype=torch.float32, device=dev) if logits is None else logits
-    probs = torch.empty((M, C), dtype=torch.float64, device=dev) if probs is None else probs
+    xq = _out(xq, (M, K), torch.int8, dev, stream, "xq")
+    sx = _out(sx, (M,), torch.float32, dev, stream, "sx")
+    logits = _out(logits, (M, C), torch.float32, dev, stream, "logits")
+    probs = _out(probs, (M, C), torch.float64, dev, stream, "probs")
     _check(_lib.w8a8_answer_head(_ptr(h), h.stride(0), rows, _ptr(answer_rows), M, _ptr(smooth), K,
                                  _ptr(w_vocab), _ptr(sw_vocab), w_vocab.shape[0], _ptr(cand), C,
                                  _ptr(xq), _ptr(sx), _ptr(logits), _ptr(probs), _ptr(err_flag),

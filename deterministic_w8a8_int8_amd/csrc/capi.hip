@@ -9,6 +9,7 @@
 
 #include "launch.h"
 #include "w8a8.h"
+#include "w8a8_diag.h"
 
 namespace {
 

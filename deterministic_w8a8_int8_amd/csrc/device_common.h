@@ -47,10 +47,14 @@ typedef __attribute__((address_space(3))) int8_t lds_i8;
 // at lds + 16*lane (global_load_lds_dwordx4; the LDS base goes through M0).
 // Issued as inline asm so that the compiler does not make later LDS reads of
 // other buffers wait for this copy; callers wait with an explicit vmcnt.
+// M0 is an input operand ("{m0}"), so the compiler writes it and knows it is
+// used.  An SALU write of M0 needs one wait state before an LDS DMA reads it;
+// the compiler's hazard check does not look inside inline asm, hence the
+// s_nop 0 ahead of the copy.
 __device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "v"(voff), "s"(gbase), "{m0}"(lds)
                  : "memory");
 }
 

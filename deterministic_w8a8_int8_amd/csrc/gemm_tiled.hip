@@ -49,6 +49,7 @@
 //     fl(fl(fl(float(acc))*sx)*sw) (+ r), rounding once per step, with no
 //     fused multiply-add (the whole file is built with -ffp-contract=off).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -112,11 +113,12 @@ struct Cfg {
 
 // One wave instruction that touches one L2 line per lane: each lane copies 4
 // bytes from gbase + voff into LDS at lds + 4*lane, a landing area nobody
-// reads.  Its only purpose is to bring the line into the XCD's L2.
+// reads.  Its only purpose is to bring the line into the XCD's L2.  M0 is
+// passed as in lds_fill16, with the same wait state.
 __device__ __forceinline__ void l2_touch4(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
-                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "v"(voff), "s"(gbase), "{m0}"(lds)
                  : "memory");
 }
 
@@ -1078,12 +1080,14 @@ const KindInfo kKinds[TILE_KINDS] = {
     {Cfg6::BM, Cfg6::BN, Cfg6::OCC, 1.07},
 };
 
-int tile_override = -1;
+// Process-wide tuning hook; an atomic so that host threads may set and read
+// it concurrently (a plan reads it once).
+std::atomic<int> tile_override{-1};
 
 }  // namespace
 
-void set_tile_override(int kind) { tile_override = kind; }
-int tile_override_value() { return tile_override; }
+void set_tile_override(int kind) { tile_override.store(kind, std::memory_order_relaxed); }
+int tile_override_value() { return tile_override.load(std::memory_order_relaxed); }
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
     (void)K;
@@ -1107,7 +1111,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
             best = c;
         }
     }
-    if (tile_override >= 0 && tile_override < TILE_KINDS) best = tile_override;
+    const int ov = tile_override_value();
+    if (ov >= 0 && ov < TILE_KINDS) best = ov;
     GemmPlan p;
     p.kind = static_cast<TileKind>(best);
     p.bm = kKinds[best].bm;

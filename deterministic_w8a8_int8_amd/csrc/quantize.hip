@@ -39,7 +39,10 @@
 //   - the row maximum is a wave64 shuffle reduction, then per-wave partial
 //     maxima through LDS (max is exact, so order does not matter);
 //   - rows longer than the register budget (K > 32768) take an exact
-//     two-pass variant that reads x twice.
+//     two-pass variant that reads x twice;
+//   - a row whose smoothed values include a NaN or an infinity (from the
+//     input, or from x/s overflowing) has no finite maximum.  Like a row
+//     index out of range, it gets sx = NaN and all codes 0.
 #include "device_common.h"
 #include "launch.h"
 
@@ -51,12 +54,19 @@ constexpr int QTHREADS = 256;   // workgroup of the exact two-pass kernel
 
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
+// Clamp a rounded quotient to the code range; a NaN quotient (possible only
+// with a given maximum that does not bound the row) gives code 0.
+__device__ __forceinline__ int8_t to_code(float q) {
+    if (!(q == q)) return 0;
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return static_cast<int8_t>(static_cast<int>(q));
+}
+
 // Exact quantisation of one smoothed value (both true divisions done).
 __device__ __forceinline__ int8_t quantize_exact(float x, float s, float scale) {
     if (scale == 0.0f) return 0;
     const float t = (x / s) / scale;
-    const float r = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
-    return static_cast<int8_t>(static_cast<int>(r));
+    return to_code(rintf(t));
 }
 
 // Fast quantisation with the proof described above; falls back to the exact
@@ -72,8 +82,7 @@ __device__ __forceinline__ int8_t quantize_fast(float x, float r, const float4* 
         const float s = reinterpret_cast<const float*>(s4)[4 * j + c];
         q = rintf((x / s) / scale);
     }
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return static_cast<int8_t>(static_cast<int>(q));
+    return to_code(q);
 }
 
 __device__ __forceinline__ float4 f4(float v) { return make_float4(v, v, v, v); }
@@ -81,6 +90,21 @@ __device__ __forceinline__ float4 f4(float v) { return make_float4(v, v, v, v); 
 __device__ __forceinline__ float absmax4(float m, float4 v) {
     return fmaxf(fmaxf(fmaxf(m, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
 }
+
+// |v| for the exact row maximum, with NaN mapped to +Inf: a row holding a
+// NaN or infinite smoothed value then has an infinite maximum (fmaxf alone
+// would drop the NaN), which marks it invalid.
+__device__ __forceinline__ float abs_nf(float v) {
+    const float a = fabsf(v);
+    return a == a ? a : __builtin_inff();
+}
+
+__device__ __forceinline__ float absmax4_nf(float m, float4 v) {
+    return fmaxf(fmaxf(fmaxf(m, abs_nf(v.x)), fmaxf(abs_nf(v.y), abs_nf(v.z))), abs_nf(v.w));
+}
+
+// A per-token maximum that yields a scale: finite and not negative (NaN fails).
+__device__ __forceinline__ bool usable_max(float a) { return a >= 0.0f && a <= 0x1.fffffep127f; }
 
 // Block-wide maximum of one float per thread (NW waves).  `red` must not be
 // reused until every thread has read the result: callers alternate buffers.
@@ -156,6 +180,7 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 
         float4 xv[NV];
         float amax_loc = 0.0f;   // this thread's approximate maximum
+        bool huge_t = false;     // an approximation that is NaN, infinite or >= 2^126
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int j = t + i * T;
@@ -164,6 +189,8 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
                 const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y,
                                               xv[i].z * rv[i].z, xv[i].w * rv[i].w);
                 amax_loc = absmax4(amax_loc, ap);
+                huge_t |= !(fabsf(ap.x) < 0x1p126f) || !(fabsf(ap.y) < 0x1p126f) ||
+                          !(fabsf(ap.z) < 0x1p126f) || !(fabsf(ap.w) < 0x1p126f);
             }
         }
         float amax = 0.0f;
@@ -172,17 +199,20 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
             // a given maximum: no reduction over the row.  A NaN or negative
             // one marks the row invalid, like a bad row index.
             amax = amax_in[m];
-            valid = ok && amax >= 0.0f;
+            valid = ok && usable_max(amax);
         } else {
             // This wave's exact maximum: the element holding it has an
             // approximation within 2^-21 of the wave's approximate maximum
             // (a shuffle reduction, no barrier), so only elements within
             // 2^-19 of it -- usually one per wave -- are divided exactly; all
             // of the wave's are when the approximations cannot be trusted
-            // (an odd smoothing value in the wave, or a maximum below 2^-96).
-            // One block-wide maximum of the exact values gives the row's.
+            // (an odd smoothing value in the wave, a maximum below 2^-96, or
+            // an approximation that is NaN, infinite or near overflow, where
+            // fl(x/s) may overflow while x*rcp(s) does not or the reverse).
+            // One block-wide maximum of the exact values gives the row's; a
+            // non-finite smoothed value makes it +Inf.
             const float amax_w = wave_max(amax_loc);
-            const bool all_exact = __any(odd_t) || !(amax_w >= 0x1p-96f);
+            const bool all_exact = __any(odd_t) || __any(huge_t) || !(amax_w >= 0x1p-96f);
             const float thresh = amax_w * (1.0f - 0x1p-19f);
             float amax_t = 0.0f;
 #pragma unroll
@@ -200,10 +230,11 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (all_exact || fabsf(xs[c] * rs[c]) >= thresh)
-                            amax_t = fmaxf(amax_t, fabsf(xs[c] / ss[c]));
+                            amax_t = fmaxf(amax_t, abs_nf(xs[c] / ss[c]));
                 }
             }
             amax = block_max<NW>(amax_t, redf[rr & 1]);
+            valid = ok && usable_max(amax);
         }
         // tiny rows (or odd smoothing values) take the exact divisions
         const bool exact = odd_t || !(amax >= 0x1p-96f);
@@ -237,18 +268,20 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 // Any K: the row is read twice (the second read usually hits L2) and every
 // element takes the exact divisions.
 // Exact max_k |fl(x[m,k]/s[k])| of one row (every element divided).
+// A NaN or infinite smoothed value makes the maximum +Inf.
 __device__ __forceinline__ float row_absmax_exact(const float4* xr, const float4* s4, int64_t K4,
                                                   float* red) {
     float amax = 0.0f;
     for (int64_t j = threadIdx.x; j < K4; j += QTHREADS) {
         const float4 a = xr[j], s = s4[j];
-        amax = absmax4(amax, make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w));
+        amax = absmax4_nf(amax, make_float4(a.x / s.x, a.y / s.y, a.z / s.z, a.w / s.w));
     }
     return block_max<QTHREADS / 64>(amax, red);
 }
 
 // The slice maximum of a row-parallel rank: amax[m] = (max with amax[m] if
-// accumulate) of row m's exact smoothed maximum; NaN for a bad row index.
+// accumulate) of row m's exact smoothed maximum; +Inf for a slice holding a
+// NaN or infinite smoothed value; NaN for a bad row index.
 __global__ __launch_bounds__(QTHREADS) void row_absmax_kernel(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t K, int accumulate, float* __restrict__ amax_out) {
@@ -274,7 +307,7 @@ __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     const int64_t K4 = K >> 2;
 
     const float amax = amax_in ? amax_in[m] : row_absmax_exact(xr, s4, K4, red);
-    const bool valid = ok && amax >= 0.0f;
+    const bool valid = ok && usable_max(amax);
     const float scale = valid ? amax / 127.0f : 0.0f;
     if (threadIdx.x == 0) sx[m] = valid ? scale : quiet_nan();
 

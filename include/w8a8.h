@@ -64,72 +64,12 @@ typedef enum {
 #define W8A8_MAX_CANDIDATES 64
 /* Largest split-K factor accepted. */
 #define W8A8_MAX_SPLITK 64
-/* w8a8_set_tile_override value that forces the column-panel kernel. */
-#define W8A8_TILE_OVERRIDE_PANEL 7
 
 /* Human-readable name of a status code (host; never NULL). */
 const char* w8a8_status_string(int status);
 
 /* Version of this ABI: major*10000 + minor*100 + patch (host). */
 int w8a8_abi_version(void);
-
-/* Tuning and test hook (host, process-wide): force the tile configuration of
- * the tiled GEMM for later calls.  -1 = automatic (the default); 0..6 pick
- * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
- * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
- * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
- * stages, 5: as 4 with the epilogue stored straight from the accumulators,
- * 6: 256x320 with 8 waves);
- * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
- * hold the rows (by default it runs for 64 < M <= 512).  It never changes a
- * result bit, only speed.
- * Returns W8A8_ERR_INVALID_ARG for other values. */
-int w8a8_set_tile_override(int kind);
-
-/*
- * Diagnostic (host, no GPU call): which kernel w8a8_gemm_splitk would run
- * for this shape, split bound and residual flag (w8a8_gemm is splitk 1),
- * under the current tile override.  out: host int32[10], filled as
- *   out[0] = 0: skinny kernel (M <= 64); rest 0.
- *   out[0] = 1: tiled kernel; out[1] tile configuration, out[2] and out[3]
- *            the tile's rows and columns, out[4] the K splits; rest 0.
- *   out[0] = 2: column-panel kernel; out[1] its configuration, out[2] row
- *            splits R, out[3] column panels P, out[4] K splits S (at most
- *            splitk), out[5] 64-byte K-blocks per split, out[6] row blocks
- *            of 16 per wave (limit), out[7] column blocks of 16 per panel
- *            (limit), out[8] staging register sets, out[9] LDS slots.
- * Returns W8A8_ERR_INVALID_ARG for an invalid shape or a NULL out.
- */
-int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, int32_t* out);
-
-/*
- * Diagnostic (not part of the layer): launch an MFMA-only kernel that runs
- * int8 MFMAs on register-resident operands, with no memory traffic, so the
- * caller can time the throughput the int8 matrix cores sustain on a given
- * kind of operand data.  operand_kind 0: v_mfma_i32_32x32x32_i8, A and B
- * uniform int8; 1: the same with A shaped like per-token-quantised
- * activations (mostly 0 and +-1), B uniform; 2 and 3: as 0 and 1 with
- * v_mfma_i32_16x16x64_i8 (two per 32x32x32 product, the same operations).
- * blocks x 512 threads run `iters` iterations.  *ops (host,
- * nullable) receives the number of int8 operations (2 per multiply-add)
- * launched.  sink: device int32, written only in the impossible case that
- * an xor of all accumulators equals a fixed constant (it keeps the work
- * alive).  Asynchronous on `stream`.
- */
-int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
-                            int64_t* ops, void* stream);
-
-/*
- * Diagnostic (not part of the layer): read `bytes` of device memory at buf
- * once, each of up to 4096 workgroups of 256 threads streaming its own
- * contiguous chunk with 16-byte nontemporal loads (1 KiB per wave
- * instruction), so the caller can time the read bandwidth HBM sustains (use
- * a buffer much larger than the 256 MB last-level cache).  buf: device, 16-byte aligned,
- * bytes a positive multiple of 16.  sink: device int32, written only in the
- * impossible case that an xor of everything read equals a fixed constant.
- * Returns W8A8_ERR_INVALID_ARG for a bad argument.  Asynchronous on `stream`.
- */
-int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* stream);
 
 /*
  * w8a8_quantize_act -- per-token int8 quantisation after a per-channel
@@ -154,7 +94,11 @@ int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* 
  * xq       device int8 [M,K] row-major, 16-byte aligned.
  * sx       device fp32 [M].
  * Alignment: x and smooth 16-byte aligned.
- * Non-finite inputs are outside the contract.
+ * Non-finite values: a row whose smoothed values x' include a NaN or an
+ * infinity (from x itself, or from x/smooth overflowing) has no finite
+ * maximum and so no scale.  It is treated like a row that cannot be read:
+ * sx[m] = quiet NaN and xq[m,:] = 0 (its GEMM outputs are then NaN).  Other
+ * rows are not affected.
  */
 int w8a8_quantize_act(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
                       const float* smooth, int64_t M, int64_t K,
@@ -291,8 +235,11 @@ int w8a8_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth
  * w8a8_row_absmax -- amax[m] = max_k |fl(x[row m, k] / smooth[k])| over this
  * K-slice, exact (every element divided).  accumulate != 0: amax[m] =
  * fmax(amax[m], that value), so successive calls over the slices of one
- * device give the global maximum.  A row index outside [0, x_rows) writes
- * NaN.  Arguments as for w8a8_quantize_act; amax device fp32 [M].
+ * device give the global maximum.  A slice holding a NaN or infinite
+ * smoothed value gives +Inf (so the global maximum marks the row invalid on
+ * every rank, as w8a8_quantize_act does on one device).  A row index
+ * outside [0, x_rows) writes NaN.  Arguments as for w8a8_quantize_act; amax
+ * device fp32 [M].
  */
 int w8a8_row_absmax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
                     const float* smooth, int64_t M, int64_t K, int accumulate, float* amax,
@@ -302,8 +249,10 @@ int w8a8_row_absmax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* 
  * w8a8_quantize_act_amax -- w8a8_quantize_act with the per-token maximum
  * given: sx[m] = fl(amax[m] / 127), q = clamp(rne(fl(fl(x/s)/sx)), -127, 127)
  * (q = 0 when sx = 0).  With amax[m] the row's own maximum this is exactly
- * w8a8_quantize_act.  amax: device fp32 [M], 4-byte aligned; a NaN or
- * negative entry (or a bad row index) gives sx = NaN and zero codes.
+ * w8a8_quantize_act.  amax: device fp32 [M], 4-byte aligned; a NaN,
+ * negative or infinite entry (or a bad row index) gives sx = NaN and zero
+ * codes.  With a finite maximum that does not bound the row, an element
+ * whose quotient is NaN gets code 0 and an infinite one +-127.
  */
 int w8a8_quantize_act_amax(const float* x, int64_t ldx, int64_t x_rows, const int32_t* row_idx,
                            const float* smooth, const float* amax, int64_t M, int64_t K, int8_t* xq,

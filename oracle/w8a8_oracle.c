@@ -27,6 +27,9 @@
  *   the per-token scale is sx = fl(amax/127) and q = rne(fl(x'/sx));
  *   rounding is round-half-to-even;
  *   a row whose sx is 0 (all zero, or amax/127 underflowing) quantises to 0;
+ *   a row whose smoothed values include a NaN or an infinity (from the
+ *   input, or from x/s overflowing) has no finite maximum and no scale: it
+ *   gets sx = NaN and all codes 0, as a row that cannot be read;
  *   the epilogue is y = fl(fl(fl((float)acc * sx) * sw) + r), left to right,
  *   with no fused multiply-add anywhere.
  *
@@ -36,6 +39,7 @@
  * over OpenMP threads; each output element is computed by exactly one thread
  * in the same scalar order, so the thread count never changes a bit.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -50,6 +54,22 @@
 /* |acc| must stay below 2^31 for int32 accumulation to be exact. */
 static const int64_t ORACLE_INT32_MAX = 2147483647LL;
 
+/* Absolute value for the row maximum, with NaN taken as +infinity, so that a
+ * row holding any non-finite smoothed value has an infinite maximum. */
+static float oracle_abs_for_max(float v) {
+    float a = fabsf(v);
+    if (a != a) return INFINITY;
+    return a;
+}
+
+/* A per-token maximum that yields a scale: not NaN, not negative, finite. */
+static int oracle_usable_max(float a) { return a >= 0.0f && a <= FLT_MAX; }
+
+/* Round the quotient t = fl(x'/sx) to a code: round half to even, clamp to
+ * [-127, 127].  A NaN quotient (only possible when a given maximum does not
+ * bound the row) gives 0; an infinite one clamps. */
+static int8_t oracle_code(float t);
+
 /* Round half to even, written out: floor, then compare the fraction with 1/2.
  * For |t| < 2^23 the subtraction t - floor(t) is exact in binary32. */
 static float oracle_round_half_even(float t) {
@@ -59,6 +79,16 @@ static float oracle_round_half_even(float t) {
     if (d < 0.5f) return f;
     /* exact tie: pick the even neighbour */
     return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+}
+
+static int8_t oracle_code(float t) {
+    if (t != t) return 0;
+    if (t >= 127.0f) return 127;
+    if (t <= -127.0f) return -127;
+    float r = oracle_round_half_even(t);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)(int)r;
 }
 
 int oracle_num_threads(void) {
@@ -88,8 +118,14 @@ int oracle_quantize_act(const float* x, int64_t ldx, const int32_t* row_idx,
         float amax = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
             float xs = xr[k] / smooth[k];
-            float ab = fabsf(xs);
+            float ab = oracle_abs_for_max(xs);
             if (ab > amax) amax = ab;
+        }
+        /* a non-finite smoothed value: no scale, all codes 0 */
+        if (!oracle_usable_max(amax)) {
+            sx[m] = NAN;
+            for (int64_t k = 0; k < K; ++k) xq[m * K + k] = 0;
+            continue;
         }
         /* step 3: per-token scale */
         float s = amax / 127.0f;
@@ -100,10 +136,7 @@ int oracle_quantize_act(const float* x, int64_t ldx, const int32_t* row_idx,
             if (s != 0.0f) {
                 float xs = xr[k] / smooth[k];
                 float t = xs / s;
-                float r = oracle_round_half_even(t);
-                if (r > 127.0f) r = 127.0f;
-                if (r < -127.0f) r = -127.0f;
-                q = (int8_t)(int)r;
+                q = oracle_code(t);
             }
             xq[m * K + k] = q;
         }
@@ -121,7 +154,8 @@ int oracle_quantize_act(const float* x, int64_t ldx, const int32_t* row_idx,
  * token scale of that global maximum.  The two steps of oracle_quantize_act
  * are therefore also given separately. */
 
-/* Steps 1+2 only: amax[m] = max_k |fl(x[m,k] / smooth[k])| over this slice. */
+/* Steps 1+2 only: amax[m] = max_k |fl(x[m,k] / smooth[k])| over this slice;
+ * +infinity when the slice holds a NaN or infinite smoothed value. */
 int oracle_row_absmax(const float* x, int64_t ldx, const int32_t* row_idx,
                       const float* smooth, int64_t M, int64_t K, float* amax_out) {
     if (!x || !smooth || !amax_out || M < 0 || K <= 0 || ldx < K) return ORACLE_ERR_ARG;
@@ -132,7 +166,7 @@ int oracle_row_absmax(const float* x, int64_t ldx, const int32_t* row_idx,
         const float* xr = x + src * ldx;
         float amax = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
-            float ab = fabsf(xr[k] / smooth[k]);
+            float ab = oracle_abs_for_max(xr[k] / smooth[k]);
             if (ab > amax) amax = ab;
         }
         amax_out[m] = amax;
@@ -141,7 +175,9 @@ int oracle_row_absmax(const float* x, int64_t ldx, const int32_t* row_idx,
 }
 
 /* Steps 3+4 with a given per-token maximum (the global one): sx = fl(amax/127)
- * and q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), q = 0 when sx = 0. */
+ * and q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), q = 0 when sx = 0.  A given
+ * maximum that is NaN, negative or infinite has no scale: sx = NaN and all
+ * codes 0. */
 int oracle_quantize_act_amax(const float* x, int64_t ldx, const int32_t* row_idx,
                              const float* smooth, const float* amax_in, int64_t M, int64_t K,
                              int8_t* xq, float* sx) {
@@ -151,6 +187,11 @@ int oracle_quantize_act_amax(const float* x, int64_t ldx, const int32_t* row_idx
     for (m = 0; m < M; ++m) {
         const int64_t src = row_idx ? (int64_t)row_idx[m] : m;
         const float* xr = x + src * ldx;
+        if (!oracle_usable_max(amax_in[m])) {
+            sx[m] = NAN;
+            for (int64_t k = 0; k < K; ++k) xq[m * K + k] = 0;
+            continue;
+        }
         float s = amax_in[m] / 127.0f;
         sx[m] = s;
         for (int64_t k = 0; k < K; ++k) {
@@ -158,10 +199,7 @@ int oracle_quantize_act_amax(const float* x, int64_t ldx, const int32_t* row_idx
             if (s != 0.0f) {
                 float xs = xr[k] / smooth[k];
                 float t = xs / s;
-                float r = oracle_round_half_even(t);
-                if (r > 127.0f) r = 127.0f;
-                if (r < -127.0f) r = -127.0f;
-                q = (int8_t)(int)r;
+                q = oracle_code(t);
             }
             xq[m * K + k] = q;
         }

@@ -10,6 +10,7 @@ Integer dot products use Python's unbounded ``int``.
 """
 from __future__ import annotations
 
+import math
 import struct
 from fractions import Fraction
 
@@ -68,11 +69,24 @@ def f32_bits(v: float) -> int:
     return struct.unpack("<I", struct.pack("<f", v))[0]
 
 
+def smoothed(x, s) -> float:
+    """fl(x/s) for binary32 x and a finite s > 0, exactly rounded; a NaN x
+    gives NaN, an infinite x the same infinity, and a quotient beyond the
+    binary32 range rounds to an infinity (IEEE overflow)."""
+    xf = float(x)
+    if math.isnan(xf) or math.isinf(xf):
+        return xf
+    return round_f32(f32(x) / f32(s))
+
+
 def quantize_row(x_row, s_row):
     """Per-token quantisation of one row, each binary32 step done exactly and
     rounded: x' = fl(x/s); amax = max|x'|; sx = fl(amax/127);
-    q = clamp(rne(fl(x'/sx)), -127, 127), q = 0 when sx = 0."""
-    xs = [round_f32(f32(x) / f32(s)) for x, s in zip(x_row, s_row)]
+    q = clamp(rne(fl(x'/sx)), -127, 127), q = 0 when sx = 0.  A row with a
+    non-finite x' has no scale: sx = NaN and every q = 0."""
+    xs = [smoothed(x, s) for x, s in zip(x_row, s_row)]
+    if any(not math.isfinite(v) for v in xs):
+        return [0] * len(xs), float("nan")
     amax = max(abs(v) for v in xs)
     sx = round_f32(Fraction(amax) / 127)
     q = []
@@ -119,15 +133,31 @@ def softmax_decimal(row, digits=40):
 def quantize_row_amax(x_row, s_row, amax):
     """Quantisation of one row with a given per-token maximum (the global one
     of a row-parallel layer), each binary32 step exact then rounded:
-    sx = fl(amax/127); q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), 0 when sx = 0."""
+    sx = fl(amax/127); q = clamp(rne(fl(fl(x/s)/sx)), -127, 127), 0 when sx = 0.
+    A maximum that is NaN, negative or infinite gives sx = NaN and every q = 0;
+    otherwise an element whose quotient is NaN gives 0 and an infinite one
+    clamps to +-127."""
+    a = float(amax)
+    if not (math.isfinite(a) and a >= 0):
+        return [0] * len(x_row), float("nan")
     sx = round_f32(f32(amax) / 127)
     q = []
     for x, s in zip(x_row, s_row):
         if sx == 0:
             q.append(0)
             continue
-        v = round_f32(f32(x) / f32(s))
-        t = Fraction(round_f32(Fraction(v) / Fraction(sx)))
+        v = smoothed(x, s)
+        if math.isnan(v):
+            q.append(0)
+            continue
+        if math.isinf(v):
+            q.append(127 if v > 0 else -127)
+            continue
+        tf = round_f32(Fraction(v) / Fraction(sx))
+        if math.isinf(tf):
+            q.append(127 if tf > 0 else -127)
+            continue
+        t = Fraction(tf)
         r = _round_half_even_int(abs(t)) * (1 if t >= 0 else -1)
         q.append(max(-127, min(127, r)))
     return q, sx

@@ -1,8 +1,8 @@
 """The C-ABI library without a GPU.
 
-These checks cover: it loads; it exports every function include/w8a8.h
-declares; and the host-side argument checks reject bad calls before any
-HIP call.  No call here reaches a kernel.  Every rejected call below fails
+These checks cover: it loads; it exports every function the headers in
+include/ declare; and the host-side argument checks reject bad calls before
+any HIP call.  No call here reaches a kernel.  Every rejected call below fails
 validation before the library touches the device.
 """
 import ctypes
@@ -12,14 +12,20 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "w8a8.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADER = os.path.join(INCLUDE, "w8a8.h")
 LIB = os.path.join(ROOT, "deterministic_w8a8_int8_amd", "libw8a8.so")
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text)))
+def declared_functions(path=None):
+    """Functions declared in one header, or in every header of include/."""
+    paths = [path] if path else [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE))
+                                 if f.endswith(".h")]
+    names = set()
+    for p in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+        names |= set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +38,7 @@ def lib():
 
 
 def test_header_declares_the_four_entry_points():
-    names = declared_functions()
+    names = declared_functions(HEADER)
     for n in ("w8a8_quantize_act", "w8a8_gemm", "w8a8_gemm_splitk", "w8a8_readout_candidates",
               "w8a8_gemm_splitk_workspace_bytes"):
         assert n in names
@@ -147,7 +153,8 @@ def test_argument_checks_reject_before_launch(lib):
 def test_binding_constants_match_the_header():
     """Every integer #define and status code of the header has the same value in the binding."""
     from deterministic_w8a8_int8_amd import binding
-    text = open(HEADER).read()
+    text = "".join(open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE))
+                   if f.endswith(".h"))
     pairs = re.findall(r"#define\s+(W8A8_[A-Z0-9_]+)\s+(-?\d+)", text)
     pairs += re.findall(r"\b(W8A8_(?:OK|ERR_[A-Z_]+))\s*=\s*(-?\d+)", text)
     assert len(pairs) >= 12

@@ -123,6 +123,78 @@ def test_quantize_extreme_values_match_oracle(K, tall):
         np.testing.assert_array_equal(host(xq), xq_o, err_msg=f"K={K} case {i + 1}")
 
 
+def _nonfinite_block(K, seed, tall):
+    """Ordinary rows mixed with rows holding a NaN, +Inf or -Inf input, a
+    finite input whose smoothed value overflows (3e38 / 0.25), and a finite
+    row just inside the range (3e38 / 1)."""
+    x, s = _quant_case(8, K, seed)
+    s[5] = np.float32(0.25)
+    s[6] = np.float32(1.0)
+    x[1, 9] = np.nan
+    x[2, K - 1] = np.inf
+    x[3, 0] = -np.inf
+    x[4, 5] = np.float32(3e38)
+    x[5, 6] = np.float32(3e38)
+    x[6, K // 2] = np.nan
+    x[6, K // 2 + 1] = np.inf
+    if tall:
+        x = np.tile(x, (140, 1))[:1100]
+    return x, s
+
+
+# Rows with a non-finite smoothed value get sx = NaN and all codes 0 on both
+# sides; their GEMM outputs are NaN, every other output is bit-exact.  K =
+# 40960 runs the two-pass kernel; tall repeats the rows over 1100 workgroups.
+@pytest.mark.parametrize("K,tall", [(1024, False), (5120, False), (17408, True), (40960, False)])
+def test_quantize_nonfinite_rows_match_oracle(K, tall):
+    say(f"quantize non-finite rows K={K} tall={tall}")
+    x, s = _nonfinite_block(K, seed=K + 3, tall=tall)
+    xq, sx = B.w8a8_quantize_act(dev(x), dev(s))
+    with np.errstate(all="ignore"):
+        xq_o, sx_o = oracle.quantize_act(x, s)
+    assert_bits_equal(host(sx), sx_o, f"K={K} sx")
+    np.testing.assert_array_equal(host(xq), xq_o)
+    assert np.isnan(sx_o[[1, 2, 3, 4, 6]]).all() and np.isfinite(sx_o[[0, 5, 7]]).all()
+    # the row-parallel steps: the slice maximum is +Inf on those rows, and the
+    # global-maximum quantisation gives the same bits as one device
+    amax = B.w8a8_row_absmax(dev(x), dev(s))
+    with np.errstate(all="ignore"):
+        amax_o = oracle.row_absmax(x, s)
+    assert_bits_equal(host(amax), amax_o, f"K={K} amax")
+    xq2, sx2 = B.w8a8_quantize_act_amax(dev(x), dev(s), amax)
+    assert_bits_equal(host(sx2), sx_o, f"K={K} sx (given maximum)")
+    np.testing.assert_array_equal(host(xq2), xq_o)
+    # GEMM over those rows
+    rng = np.random.default_rng(K)
+    N = 96
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    r = rng.standard_normal((x.shape[0], N), dtype=np.float32)
+    got = host(B.w8a8_gemm(xq, sx, dev(w), dev(sw), residual=dev(r)))
+    with np.errstate(all="ignore"):
+        want = oracle.gemm(xq_o, sx_o, w, sw, r)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert_bits_equal(got[fin], want[fin], f"K={K} gemm")
+
+
+def test_quantize_given_maximum_nonfinite_elements():
+    # A finite given maximum over rows holding NaN / +-Inf elements: NaN -> 0,
+    # +-Inf -> +-127 on both sides; NaN, negative and infinite maxima give an
+    # invalid row.
+    K = 256
+    x, s = _quant_case(6, K, seed=21)
+    x[1, 3], x[2, 4], x[3, 5] = np.nan, np.inf, -np.inf
+    amax = np.array([4.0, 4.0, 4.0, 4.0, np.nan, np.inf], np.float32)
+    amax[0] = -1.0
+    xq, sx = B.w8a8_quantize_act_amax(dev(x), dev(s), dev(amax))
+    with np.errstate(all="ignore"):
+        xq_o, sx_o = oracle.quantize_act_amax(x, s, amax)
+    assert_bits_equal(host(sx), sx_o, "sx")
+    np.testing.assert_array_equal(host(xq), xq_o)
+    assert xq_o[1, 3] == 0 and xq_o[2, 4] == 127 and xq_o[3, 5] == -127
+
+
 def test_quantize_row_gather_and_bad_index():
     x, s = _quant_case(40, 512, seed=5)
     idx = np.array([39, 0, 17, 17, 5, -1, 40, 2], np.int32)

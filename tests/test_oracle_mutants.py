@@ -31,6 +31,7 @@ PINS = [
     pins.test_golden_tiny_layer,
     pins.test_readout_equals_gemm_columns_and_flags_bad_ids,
     pins.test_quantize_scale_and_quotient_bruteforce_many_rows,
+    pins.test_quantize_nonfinite_rows_bruteforce,
 ]
 
 # (name, [(old, new), ...], extra gcc flags)
@@ -39,7 +40,9 @@ MUTANTS = [
     ("reciprocal instead of divide",
      [("float xs = xr[k] / smooth[k];", "float xs = xr[k] * (1.0f / smooth[k]);")], []),
     ("scale by multiply with 1/127", [("amax / 127.0f", "amax * (1.0f / 127.0f)")], []),
-    ("signed max instead of abs max", [("float ab = fabsf(xs);", "float ab = xs;")], []),
+    ("signed max instead of abs max", [("float ab = oracle_abs_for_max(xs);", "float ab = xs;")], []),
+    ("NaN dropped from the row maximum", [("if (a != a) return INFINITY;", "")], []),
+    ("infinite maximum used as a scale", [("if (!oracle_usable_max(amax)) {", "if (amax != amax) {")], []),
     ("quotient by multiply with 1/sx", [("float t = xs / s;", "float t = xs * (1.0f / s);")], []),
     ("ties away from zero",
      [("return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;", "return (f >= 0.0f) ? f + 1.0f : f;")], []),

@@ -125,6 +125,48 @@ def test_quantize_scale_and_quotient_bruteforce_many_rows():
         np.testing.assert_array_equal(xq[m].astype(np.int64), np.array(q_want), err_msg=f"row {m}")
 
 
+def _nonfinite_rows():
+    """Rows of every non-finite kind next to ordinary ones: NaN, +Inf, -Inf
+    inputs, a finite input whose smoothed value overflows (3e38 / 0.25), and
+    a finite one just inside the range (3e38 / 1)."""
+    rng = np.random.default_rng(77)
+    K = 64
+    x = rng.standard_normal((8, K)).astype(np.float32)
+    s = rng.uniform(0.5, 4.0, K).astype(np.float32)
+    s[5] = np.float32(0.25)
+    s[6] = np.float32(1.0)
+    x[1, 9] = np.nan
+    x[2, 0] = np.inf
+    x[3, 63] = -np.inf
+    x[4, 5] = np.float32(3e38)     # / 0.25 overflows
+    x[5, 6] = np.float32(3e38)     # / 1 stays finite: an ordinary (huge) row
+    x[6, 9] = np.nan
+    x[6, 10] = np.inf
+    return x, s
+
+
+def test_quantize_nonfinite_rows_bruteforce():
+    # A row with a non-finite smoothed value has no scale (the reading: like
+    # a row that cannot be read): sx = NaN, all codes 0.  Every row, finite
+    # or not, against the exact-rational reference; the other rows do not
+    # change.
+    x, s = _nonfinite_rows()
+    xq, sx = oracle.quantize_act(x, s)
+    for m in range(x.shape[0]):
+        q_want, sx_want = brute.quantize_row(x[m], s)
+        if math.isnan(sx_want):
+            assert np.isnan(sx[m]), m
+        else:
+            assert brute.f32_bits(sx_want) == int(bits(sx[m])), m
+        np.testing.assert_array_equal(xq[m].astype(np.int64), np.array(q_want), err_msg=f"row {m}")
+    assert [m for m in range(8) if np.isnan(sx[m])] == [1, 2, 3, 4, 6]
+    assert sx[5] > 0 and xq[5, 6] == 127
+    ok = [0, 5, 7]
+    xq_ok, sx_ok = oracle.quantize_act(x[ok], s)
+    np.testing.assert_array_equal(xq[ok], xq_ok)
+    np.testing.assert_array_equal(bits(sx[ok]), bits(sx_ok))
+
+
 def test_quantize_column_order_invariance():
     d = synth.tiny_linear()
     x, s = d["x"], d["smooth"]

@@ -57,6 +57,38 @@ def test_quantize_with_larger_maximum_matches_bruteforce(factor):
         assert np.abs(xq.astype(np.int32)).max() <= 64
 
 
+def test_nonfinite_slices_and_maxima():
+    # A slice with a NaN or infinite smoothed value has an infinite maximum,
+    # so the global MAX is infinite and every rank's row is invalid (sx =
+    # NaN, codes 0), as on one device.  A given maximum that is NaN,
+    # negative or infinite is invalid too.  With a finite given maximum, a
+    # NaN element quantises to 0 and an infinite one to +-127.
+    rng = np.random.default_rng(9)
+    K = 64
+    x = rng.standard_normal((6, K)).astype(np.float32)
+    s = rng.uniform(0.5, 4.0, K).astype(np.float32)
+    x[1, 3] = np.nan
+    x[2, 4] = -np.inf
+    amax = oracle.row_absmax(x, s)
+    assert np.isinf(amax[1]) and np.isinf(amax[2]) and np.isfinite(amax[[0, 3, 4, 5]]).all()
+    given = amax.copy()
+    given[3] = np.nan
+    given[4] = np.float32(-1.0)
+    given[5] = np.inf
+    xq, sx = oracle.quantize_act_amax(x, s, given)
+    assert np.isnan(sx[1:]).all() and not xq[1:].any()
+    xq_full, sx_full = oracle.quantize_act(x, s)
+    assert np.isnan(sx_full[[1, 2]]).all() and not xq_full[[1, 2]].any()
+    # finite given maxima over rows holding non-finite elements
+    fin = np.full(6, np.float32(4.0))
+    xq, sx = oracle.quantize_act_amax(x, s, fin)
+    for m in range(6):
+        q, sxb = brute.quantize_row_amax(x[m], s, fin[m])
+        assert sx[m] == np.float32(sxb)
+        assert list(xq[m]) == q, m
+    assert xq[1, 3] == 0 and xq[2, 4] == -127
+
+
 def test_zero_maximum_gives_zero_codes():
     x, s = _rows(4, 3, 64)
     xq, sx = oracle.quantize_act_amax(x, s, np.zeros(3, np.float32))
