@@ -28,6 +28,7 @@ W8A8_MAX_K = 133120
 W8A8_MAX_CANDIDATES = 64
 W8A8_MAX_SPLITK = 64
 W8A8_TILE_OVERRIDE_PANEL = 7
+W8A8_NOALLOC_SCRATCH_BYTES = 67108864
 
 # Every symbol the headers in include/ declare (w8a8.h, w8a8_diag.h), with its
 # ctypes signature.
@@ -43,6 +44,7 @@ SIGNATURES = {
     "w8a8_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
     "w8a8_gemm_splitk": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
+    "w8a8_gemm_splitk_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "w8a8_readout_candidates": (_I32, [_P, _P, _I64, _I64, _P, _P, _I64, _P, _I64, _P, _P, _P]),
     "w8a8_candidate_softmax": (_I32, [_P, _I64, _I64, _P, _P]),
     "w8a8_requantize_q8_0": (_I32, [_P, _P, _P, _I64, _I64, _P, _P, _P]),
@@ -238,6 +240,17 @@ def w8a8_gemm_splitk(xq, sx, w, sw, splitk, residual=None, y=None, workspace=Non
                                  M, N, K, int(splitk), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "w8a8_gemm_splitk")
+    return y
+
+
+def w8a8_gemm_splitk_noalloc(xq, sx, w, sw, splitk, residual=None, y=None, stream=None):
+    """w8a8_gemm_splitk with the library's own split-K scratch: the library
+    allocates nothing (y is allocated here only when the caller passes none)."""
+    M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
+    y = _out(y, (M, N), torch.float32, xq.device, stream, "y")
+    _check(_lib.w8a8_gemm_splitk_noalloc(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y),
+                                         M, N, K, int(splitk), _stream(stream)),
+           "w8a8_gemm_splitk_noalloc")
     return y
 
 

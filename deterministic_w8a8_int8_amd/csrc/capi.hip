@@ -4,8 +4,10 @@
 // include/w8a8.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 #include "w8a8.h"
@@ -100,6 +102,36 @@ int run_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw
         return hip_status(w8a8::launch_panel(a, pp, workspace, stream));
     const GemmPlan plan = w8a8::plan_gemm(M, N, K, splitk);
     return hip_status(w8a8::launch_gemm_tiled(a, plan, workspace, stream));
+}
+
+// ---- split-K scratch of the allocation-free entry point.  One array per
+// GPU the library runs on, held until the process ends.  In host code the
+// array's name is only a stand-in for it: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.
+static_assert(W8A8_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) static int8_t scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W8A8_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W8A8_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return W8A8_OK;
 }
 
 }  // namespace
@@ -203,6 +235,21 @@ int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const f
     }
     return run_gemm(xq, sx, w, sw, residual, y, M, N, K, splitk, workspace,
                     static_cast<hipStream_t>(stream));
+}
+
+int w8a8_gemm_splitk_noalloc(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                             const float* residual, float* y, int64_t M, int64_t N, int64_t K, int splitk,
+                             void* stream) {
+    if (splitk < 1 || splitk > W8A8_MAX_SPLITK) return W8A8_ERR_INVALID_ARG;
+    if (const int rc = check_gemm_args(xq, sx, w, sw, residual, y, M, N, K)) return rc;
+    if (M == 0 || N == 0) return W8A8_OK;
+    void* ws = nullptr;
+    if (splitk > 1) {
+        if (w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) > W8A8_NOALLOC_SCRATCH_BYTES)
+            return W8A8_ERR_WORKSPACE;
+        if (const int rc = scratch_address(&ws)) return rc;
+    }
+    return run_gemm(xq, sx, w, sw, residual, y, M, N, K, splitk, ws, static_cast<hipStream_t>(stream));
 }
 
 int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_t K,

@@ -165,6 +165,34 @@ int w8a8_gemm_splitk(const int8_t* xq, const float* sx, const int8_t* w, const f
                      const float* residual, float* y, int64_t M, int64_t N, int64_t K,
                      int splitk, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's own split-K scratch (64 MiB per GPU), the most
+ * w8a8_gemm_splitk_noalloc accepts. */
+#define W8A8_NOALLOC_SCRATCH_BYTES 67108864
+
+/*
+ * w8a8_gemm_splitk_noalloc -- w8a8_gemm_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and result bits as
+ * w8a8_gemm_splitk, without the workspace: the int32 partials go to a
+ * scratch array of W8A8_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates nothing.
+ * Its first call on a device looks up that device's array (a runtime
+ * symbol query, no allocation); later calls do no host-side set-up.
+ *
+ * Returns W8A8_ERR_WORKSPACE when
+ * w8a8_gemm_splitk_workspace_bytes(M, N, K, splitk) exceeds
+ * W8A8_NOALLOC_SCRATCH_BYTES (e.g. 256 x 5120 at splitk 8 is 42 MB and fits;
+ * 8192 x 5120 at splitk 2 is 336 MB and does not: use w8a8_gemm_splitk).
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (nothing in it needs clearing: each chunk overwrites
+ * its whole slice).  Calls that overlap in time on one GPU (on different
+ * streams, or from several host threads) therefore race and must be
+ * serialised by the caller.
+ */
+int w8a8_gemm_splitk_noalloc(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                             const float* residual, float* y, int64_t M, int64_t N, int64_t K,
+                             int splitk, void* stream);
+
 /*
  * w8a8_readout_candidates -- candidate-only lm_head read-out.  The review
  * page, section "Compute shared evidence once", keeps the read-out to the
