@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw8a8.so")
 
-SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "gemm_panel.hip", "softmax.hip", "requant.hip", "probes.hip", "capi.hip"]
+SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "gemm_panel.hip", "softmax.hip", "answer_head.hip", "requant.hip", "probes.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,174 @@
+// The answer head in one launch: gather the hidden row at an answer
+// position, quantise it, score the candidate vocabulary rows and turn the
+// scores into probabilities.
+//
+// The review page "StartLux-Prism: Fast, exact inference for
+// StartLux-Decision models on NVIDIA GPUs", section "Compute shared evidence
+// once", confines the read-out of the last layer to the answer positions;
+// the dsiab.com post on moving decision models from vLLM to Prism, section
+// "方案", scores only the candidate tokens and normalises among them.  Each
+// step is the library's own definition, computed by the same device code as
+// the separate entry points, so every result is bit-identical to calling
+// w8a8_quantize_act (with row_idx), w8a8_readout_candidates and
+// w8a8_candidate_softmax in turn:
+//   - one workgroup per answer row holds the row in registers and quantises
+//     it with quantize_row_regs (the per-token quantisation of quantize.hip);
+//   - a candidate logit is the exact int32 dot product of the row's codes
+//     with the candidate's weight row (v_dot4_i32_i8, four int8 products and
+//     an int32 addition, no saturation: K * 127^2 < 2^31 keeps every partial
+//     sum exact), summed over the workgroup in int32 (exact, so the order
+//     does not matter), then the fixed epilogue fl(fl(float(acc) * sx) * sw);
+//   - an id outside [0, V) gives a quiet NaN logit and sets bit 0 of
+//     err_flag, as the read-out does;
+//   - wave 0 then runs candidate_softmax_wave (the softmax kernel's code) on
+//     the logits.
+// The weight rows of the first candidates are requested before the
+// quantisation starts, so their latency overlaps the row's; the workgroup
+// then walks the candidates in groups of AH_GROUP, each group's weights in
+// flight while the previous group is reduced.
+#include "device_common.h"
+#include "launch.h"
+#include "quantize_row.h"
+#include "softmax_row.h"
+
+namespace w8a8 {
+
+namespace {
+
+constexpr int AH_GROUP = 4;   // candidates whose weight rows are loaded together
+
+template <int NV, int T>
+__global__ __launch_bounds__(T) void answer_head_kernel(
+    const float* __restrict__ h, int64_t ldh, int64_t h_rows, const int32_t* __restrict__ rows,
+    const float* __restrict__ smooth, int64_t K, const int8_t* __restrict__ w, const float* __restrict__ sw,
+    int64_t V, const int32_t* __restrict__ cand, int C, int8_t* __restrict__ xq, float* __restrict__ sx,
+    float* __restrict__ logits, double* __restrict__ probs, int32_t* __restrict__ err_flag) {
+    constexpr int NW = T / 64;
+    __shared__ float red[NW];
+    __shared__ int32_t part[2][AH_GROUP][NW];
+    __shared__ float lg[64];
+    const int64_t m = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int K4 = static_cast<int>(K >> 2);
+
+    // candidate ids: lane c of every wave holds id c (C <= 64); an id
+    // outside [0, V) reads row 0 and yields NaN
+    const int id_raw = lane < C ? cand[m * C + lane] : 0;
+    const bool id_ok = id_raw >= 0 && id_raw < V;
+    const int id_lane = id_ok ? id_raw : 0;
+
+    // weight words of the candidates of group g: thread t's word j = t + T*i
+    // of row id holds the int8 weights of columns 4j .. 4j+3
+    uint32_t wv[AH_GROUP][NV];
+    auto load_group = [&](int g0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < AH_GROUP; ++c) {
+            const int id = __shfl(id_lane, min(g0 + c, 63), 64);
+            const uint32_t* wr = reinterpret_cast<const uint32_t*>(w + static_cast<int64_t>(id) * K);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int j = t + i * T;
+                wv[c][i] = (j < K4 && g0 + c < C) ? wr[j] : 0u;
+            }
+        }
+    };
+    if (C > 0) load_group(0);
+
+    // the answer row, quantised (bits of quantize_rows_reg)
+    int64_t src;
+    const bool ok = source_row(rows, m, h_rows, &src);
+    const float4* s4 = reinterpret_cast<const float4*>(smooth);
+    float4 rv[NV];
+    bool odd_t;
+    row_reciprocals<NV, T>(s4, K4, rv, odd_t);
+    float4 xv[NV];
+    load_row<NV, T>(reinterpret_cast<const float4*>(h + src * ldh), K4, xv);
+    uint32_t q[NV];
+    bool valid;
+    const float scale = quantize_row_regs<NV, T, false>(xv, rv, odd_t, s4, K4, ok, 0.0f, red, q, valid);
+    const float sxm = valid ? scale : quiet_nan();
+    if (t == 0) sx[m] = sxm;
+    uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int j = t + i * T;
+        if (j < K4) qr[j] = q[i];
+    }
+
+    // candidate logits, AH_GROUP at a time
+    for (int g0 = 0, gi = 0; g0 < C; g0 += AH_GROUP, ++gi) {
+        int32_t dot[AH_GROUP];
+#pragma unroll
+        for (int c = 0; c < AH_GROUP; ++c) {
+            int32_t a = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                a = __builtin_amdgcn_sdot4(static_cast<int>(q[i]), static_cast<int>(wv[c][i]), a, false);
+            dot[c] = a;
+        }
+        if (g0 + AH_GROUP < C) load_group(g0 + AH_GROUP);   // next group in flight
+#pragma unroll
+        for (int c = 0; c < AH_GROUP; ++c) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) dot[c] += __shfl_xor(dot[c], off, 64);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int c = 0; c < AH_GROUP; ++c) part[gi & 1][c][wave] = dot[c];
+        }
+        // lane l < AH_GROUP of wave 0 finishes candidate g0 + l: its id and
+        // validity, shuffled from lane g0 + l while every lane is active
+        const int src_lane = min(g0 + (lane & (AH_GROUP - 1)), 63);
+        const int id = __shfl(id_lane, src_lane, 64);
+        const bool okc = __shfl(static_cast<int>(id_ok), src_lane, 64) != 0;
+        __syncthreads();
+        if (wave == 0 && lane < AH_GROUP && g0 + lane < C) {
+            int32_t acc = 0;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) acc += part[gi & 1][lane][v];
+            const int c = g0 + lane;
+            const float l = okc ? scale_acc(acc, sxm, sw[id]) : quiet_nan();
+            lg[c] = l;
+            logits[m * C + c] = l;
+            if (!okc && err_flag) atomicOr(err_flag, 1);
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && C > 0) {
+        const bool live = lane < C;
+        const double p = candidate_softmax_wave(live ? lg[lane] : 0.0f, live, C);
+        if (live) probs[m * C + lane] = p;
+    }
+}
+
+template <int NV, int T>
+hipError_t launch_t(const AnswerHeadArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((answer_head_kernel<NV, T>), dim3(static_cast<unsigned>(a.M)), dim3(T), 0, stream, a.h,
+                       a.ldh, a.h_rows, a.rows, a.smooth, a.K, a.w, a.sw, a.V, a.cand, static_cast<int>(a.C),
+                       a.xq, a.sx, a.logits, a.probs, a.err_flag);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool answer_head_fused_fits(int64_t K) { return K <= 18432; }
+
+hipError_t launch_answer_head(const AnswerHeadArgs& a, hipStream_t stream) {
+    if (a.M == 0) return hipSuccess;
+    const int64_t n256 = (a.K + 1023) / 1024;   // float4 per thread with 256 threads
+    const int64_t n512 = (a.K + 2047) / 2048;   // ... with 512 threads
+    if (n256 <= 1) return launch_t<1, 256>(a, stream);
+    if (n256 <= 2) return launch_t<2, 256>(a, stream);
+    if (n256 <= 3) return launch_t<3, 256>(a, stream);
+    if (n256 <= 4) return launch_t<4, 256>(a, stream);
+    if (n256 <= 5) return launch_t<5, 256>(a, stream);
+    if (n256 <= 6) return launch_t<6, 256>(a, stream);
+    if (n512 <= 4) return launch_t<4, 512>(a, stream);
+    if (n512 <= 5) return launch_t<5, 512>(a, stream);
+    if (n512 <= 6) return launch_t<6, 512>(a, stream);
+    if (n512 <= 8) return launch_t<8, 512>(a, stream);
+    if (n512 <= 9) return launch_t<9, 512>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace w8a8

@@ -350,6 +350,11 @@ int w8a8_answer_head(const float* h, int64_t ldh, int64_t h_rows, const int32_t*
     if (const int rc = check_softmax_args(logits, M, C, probs)) return rc;
     if (M == 0) return W8A8_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (w8a8::answer_head_fused_fits(K)) {
+        const w8a8::AnswerHeadArgs a{h, ldh, h_rows, answer_rows, M, smooth, K, w_vocab, sw_vocab, V,
+                                     cand, C, xq, sx, logits, probs, err_flag};
+        return hip_status(w8a8::launch_answer_head(a, s));
+    }
     const w8a8::QuantArgs q{h, ldh, h_rows, answer_rows, smooth, M, K, xq, sx, nullptr};
     if (const int rc = hip_status(w8a8::launch_quantize(q, s))) return rc;
     if (C == 0) return W8A8_OK;

@@ -120,6 +120,32 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream);
 hipError_t launch_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth, int64_t N,
                                   int64_t K, int8_t* wq, float* sw, hipStream_t stream);
 
+// The answer head in one launch (answer_head.hip): quantise the hidden rows
+// rows[0..M) of h, score the C candidates of each, candidate softmax; the
+// same bits as launch_quantize + launch_skinny (gather/owner mode) +
+// launch_candidate_softmax.  Needs K <= 18432 (answer_head_fused_fits).
+struct AnswerHeadArgs {
+    const float* h;
+    int64_t ldh;
+    int64_t h_rows;
+    const int32_t* rows;
+    int64_t M;
+    const float* smooth;
+    int64_t K;
+    const int8_t* w;
+    const float* sw;
+    int64_t V;
+    const int32_t* cand;
+    int64_t C;
+    int8_t* xq;
+    float* sx;
+    float* logits;
+    double* probs;
+    int32_t* err_flag;
+};
+bool answer_head_fused_fits(int64_t K);
+hipError_t launch_answer_head(const AnswerHeadArgs& a, hipStream_t stream);
+
 // Candidate softmax in binary64, one fixed operation sequence (softmax.hip):
 // probs[m, c] for c < C <= 64; rows with a non-finite logit give NaN.
 hipError_t launch_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs,

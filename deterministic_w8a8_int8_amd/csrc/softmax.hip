@@ -33,59 +33,21 @@
 // (C + 6) units in the last place.
 #include "device_common.h"
 #include "launch.h"
+#include "softmax_row.h"
 
 namespace w8a8 {
 
 namespace {
 
-constexpr double LN2_HI = 0x1.62e42fefa0000p-1;
-constexpr double LN2_LO = 0x1.cf79abc9e3b3ap-40;
-constexpr double INV_LN2 = 0x1.71547652b82fep+0;
-
-__device__ __forceinline__ double exp64_nonpositive(double z) {
-    if (z < -746.0) return 0.0;  // below half the smallest subnormal
-    const double k = rint(z * INV_LN2);
-    const double r = (z - k * LN2_HI) - k * LN2_LO;
-    // 1/n!, n = 13 .. 0
-    constexpr double c[14] = {
-        0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26,
-        0x1.27e4fb7789f5cp-22, 0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16,
-        0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10, 0x1.1111111111111p-7,
-        0x1.5555555555555p-5,  0x1.5555555555555p-3,  0x1.0000000000000p-1,
-        0x1.0000000000000p+0,  0x1.0000000000000p+0};
-    double p = c[0];
-#pragma unroll
-    for (int n = 1; n < 14; ++n) p = fma(p, r, c[n]);
-    return ldexp(p, static_cast<int>(k));
-}
-
 // One wave per row; lane c holds candidate c (C <= 64).
 __global__ __launch_bounds__(64) void candidate_softmax_kernel(const float* __restrict__ logits,
                                                                int64_t C, double* __restrict__ probs) {
-    __shared__ double e_s[64];
     const int64_t m = blockIdx.x;
     const int c = threadIdx.x;
     const bool live = c < C;
     const float lf = live ? logits[m * C + c] : 0.0f;
-    const bool bad = live && !isfinite(lf);
-    const double l = static_cast<double>(lf);
-    // exact maximum over the live lanes
-    double mx = live ? l : -INFINITY;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off, 64));
-    const bool row_bad = __any(bad);
-    const double e = live ? exp64_nonpositive(l - mx) : 0.0;
-    e_s[c] = e;
-    __syncthreads();
-    // the sum in candidate order, by one lane, then broadcast through LDS
-    if (c == 0) {
-        double s = e_s[0];
-        for (int64_t j = 1; j < C; ++j) s += e_s[j];
-        e_s[0] = s;  // e_0 is already in this lane's register
-    }
-    __syncthreads();
-    const double S = e_s[0];
-    if (live) probs[m * C + c] = row_bad ? static_cast<double>(quiet_nan()) : e / S;
+    const double p = candidate_softmax_wave(lf, live, static_cast<int>(C));
+    if (live) probs[m * C + c] = p;
 }
 
 }  // namespace

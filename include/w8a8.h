@@ -328,13 +328,15 @@ int w8a8_epilogue_int32(const int32_t* parts, int S, const float* sx, const floa
 int w8a8_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs, void* stream);
 
 /*
- * w8a8_answer_head -- the answer read-out end to end, in three launches on
- * `stream`: w8a8_quantize_act of the hidden rows answer_rows[0..M) of h
- * (the answer positions; review page, section "Compute shared evidence
- * once"), w8a8_readout_candidates on them, and w8a8_candidate_softmax.
- * Every result is bit-identical to calling those three entry points in
- * turn with the same arguments.  All arguments are checked before the first
- * launch; a rejected call writes nothing.
+ * w8a8_answer_head -- the answer read-out end to end on `stream`:
+ * w8a8_quantize_act of the hidden rows answer_rows[0..M) of h (the answer
+ * positions; review page, section "Compute shared evidence once"),
+ * w8a8_readout_candidates on them, and w8a8_candidate_softmax.  For
+ * K <= 18432 the three steps run as one kernel (one workgroup per answer
+ * row); above it, as the three launches.  Every result is bit-identical to
+ * calling those three entry points in turn with the same arguments.  All
+ * arguments are checked before the first launch; a rejected call writes
+ * nothing.
  *
  * h, ldh, h_rows   device fp32 hidden states [h_rows, ldh] (as x of
  *                  w8a8_quantize_act); answer_rows device int32 [M], required.

@@ -149,3 +149,61 @@ def test_answer_head_bad_candidate_marks_row():
     assert int(host(err)[0]) & 1
     assert np.isnan(lg[1, 3]) and np.isnan(p[1]).all()
     assert np.isfinite(p[[0, 2]]).all()
+
+
+def _same_or_both_nan(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return bool(np.all((a.view(np.uint8).reshape(a.shape + (-1,)) == b.view(np.uint8).reshape(b.shape + (-1,))).all(-1)
+                       | (np.isnan(a) & np.isnan(b))))
+
+
+# The answer head runs as one kernel for K <= 18432 (256 threads up to K =
+# 6144, 512 above) and as three launches beyond.  Every output (quantised
+# rows, token scales, logits, probabilities) must equal the separate calls
+# bit for bit, with bad row indices and bad candidate ids, several candidate
+# groups (C up to 64) and many answer rows; valid rows' logits must equal the
+# oracle's.
+@pytest.mark.parametrize("K,C,M", [(256, 1, 1), (1024, 4, 3), (5120, 4, 1), (5120, 7, 70), (6144, 64, 5),
+                                   (8192, 5, 9), (17408, 4, 3), (40960, 4, 2)])
+def test_answer_head_fused_matches_separate_calls(K, C, M):
+    say(f"answer head K={K} C={C} M={M}")
+    V = 3000
+    rng = np.random.default_rng(K + C + M)
+    h = rng.standard_normal((M + 7, K)).astype(np.float32)
+    h[:, rng.choice(K, max(1, K // 100), replace=False)] *= np.float32(30.0)
+    smooth = rng.uniform(0.5, 4.0, K).astype(np.float32)
+    w = rng.integers(-127, 128, (V, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, V).astype(np.float32)
+    rows = rng.integers(0, M + 7, M).astype(np.int32)
+    cand = np.stack([rng.choice(V, C, replace=False) for _ in range(M)]).astype(np.int32)
+    if M > 1:
+        rows[1] = -1                    # a row that cannot be read: sx NaN, codes 0, NaN logits
+        cand[0, C - 1] = V + 5          # a candidate outside the vocabulary
+    d = {k: dev(v) for k, v in dict(h=h, rows=rows, smooth=smooth, w=w, sw=sw, cand=cand).items()}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    logits, probs = B.w8a8_answer_head(d["h"], d["rows"], d["smooth"], d["w"], d["sw"], d["cand"], xq=xq, sx=sx,
+                                       err_flag=err)
+    err2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xq2, sx2 = B.w8a8_quantize_act(d["h"], d["smooth"], row_idx=d["rows"])
+    lg2 = B.w8a8_readout_candidates(xq2, sx2, d["w"], d["sw"], d["cand"], err_flag=err2)
+    pr2 = B.w8a8_candidate_softmax(lg2)
+    assert np.array_equal(host(xq), host(xq2))
+    assert _same_or_both_nan(host(sx), host(sx2))
+    assert _same_or_both_nan(host(logits), host(lg2))
+    assert _same_or_both_nan(host(probs), host(pr2))
+    assert int(host(err)[0]) == int(host(err2)[0]) == (1 if M > 1 else 0)
+    ok = rows >= 0
+    oxq, osx = oracle.quantize_act(h[rows[ok]], smooth)
+    assert np.array_equal(host(xq)[ok], oxq)
+    good = cand.copy()
+    good[good >= V] = 0
+    olg, _ = oracle.readout_candidates(oxq, osx, w, sw, good[ok])
+    lg = host(logits)[ok]
+    valid_c = (cand[ok] < V)
+    assert_bits_equal(lg[valid_c], olg[valid_c], "fused answer head logits vs oracle")
+    rows_ok = valid_c.all(1)
+    if rows_ok.any():
+        np.testing.assert_allclose(host(probs)[ok][rows_ok], oracle.candidate_softmax(olg[rows_ok]),
+                                   rtol=2.0 ** -44, atol=0)
