@@ -22,7 +22,14 @@ traffic (uniform int8, and activation-like A; 32x32x32 and 16x16x64 MFMAs),
 measured in the same run; ``roofline.frac_of_sustained_ceiling`` relates
 the GEMM to the ceiling of its own MFMA form on activation-like operands.
 ``cpu_baseline`` is the CPU oracle on a bounded sample of the same step
-(rank 0 only).
+(rank 0 only): the first R tokens through both layers and the read-out of
+token R-1, on all host threads and single-threaded, with the CPU model.
+``parity`` compares the GPU's outputs of those rows with the oracle's, bit
+for bit (the answer head is run once more on row R-1 for it).
+``large_m_config4`` times the batch-invariance stress batch (64 requests,
+M = 17664 with padding) through 5120 -> 15360 at split-K 1 and 4.
+``mid_m`` reports each mid-sized projection both with events around every
+launch and as 30 launches back to back.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--splitk S]
 """
@@ -115,32 +122,91 @@ class Timer:
         self.pairs = {}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(gu, dn, head, cand, seconds):
     """The CPU oracle, untuned, on the first R rows of both layers plus the
-    answer read-out; R grows until the sample costs about `seconds`."""
+    answer read-out of row R-1; R grows until the sample costs about
+    `seconds` on all threads.  Also the same work single-threaded on a
+    smaller sample.  Returns (baseline, outputs): the oracle's outputs of the
+    sample are what the GPU's rows are checked against."""
     import oracle
 
     def work(R):
         t0 = time.perf_counter()
         xq, sx = oracle.quantize_act(gu["x"][:R], gu["smooth"])
-        oracle.gemm(xq, sx, gu["w"], gu["sw"])
-        xq, sx = oracle.quantize_act(dn["x"][:R], dn["smooth"])
-        y = oracle.gemm(xq, sx, dn["w"], dn["sw"], dn["r"][:R])
-        xq, sx = oracle.quantize_act(y[-1:], head["smooth"])
-        logits, _ = oracle.readout_candidates(xq, sx, head["w"], head["sw"], cand)
-        oracle.candidate_softmax(logits)
-        return time.perf_counter() - t0
+        y1 = oracle.gemm(xq, sx, gu["w"], gu["sw"])
+        xq2, sx2 = oracle.quantize_act(dn["x"][:R], dn["smooth"])
+        y2 = oracle.gemm(xq2, sx2, dn["w"], dn["sw"], dn["r"][:R])
+        xq3, sx3 = oracle.quantize_act(y2[-1:], head["smooth"])
+        logits, _ = oracle.readout_candidates(xq3, sx3, head["w"], head["sw"], cand)
+        probs = oracle.candidate_softmax(logits)
+        dt = time.perf_counter() - t0
+        return dt, {"R": R, "xq1": xq, "sx1": sx, "y1": y1, "xq2": xq2, "sx2": sx2, "y2": y2,
+                    "logits": logits, "probs": probs}
 
+    K1, N1, K2, N2 = gu["K"], gu["N"], dn["K"], dn["N"]
+    ops = lambda R: 2.0 * R * (N1 * K1 + N2 * K2) + 2.0 * cand.size * head["K"]
     threads = oracle.num_threads()
     R = threads
-    dt = work(R)
+    dt, _ = work(R)
     R = int(min(gu["M"], max(threads, threads * round(seconds / max(dt, 1e-3)))))
-    dt = work(R)
-    K1, N1, K2, N2 = gu["K"], gu["N"], dn["K"], dn["N"]
-    ops = 2.0 * R * (N1 * K1 + N2 * K2) + 2.0 * cand.size * head["K"]
-    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"first {R} of {gu['M']} tokens through both layers plus the read-out "
-                      f"({ops / 1e9:.1f} GOP in {dt:.2f} s, int64 scalar loops)"}
+    dt, out = work(R)
+    # single thread, on a sample about 1/threads as large
+    R1 = max(1, R // max(threads, 1))
+    oracle.set_num_threads(1)
+    try:
+        dt1, _ = work(R1)
+    finally:
+        oracle.set_num_threads(threads)
+    base = {"value": round(ops(R) / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
+            "single_thread_TOPS": round(ops(R1) / dt1 / 1e12, 6),
+            "sample": f"first {R} of {gu['M']} tokens through both layers plus the read-out of row {R - 1} "
+                      f"({ops(R) / 1e9:.1f} GOP in {dt:.2f} s on {threads} threads, int64 scalar loops); "
+                      f"single thread: first {R1} tokens ({ops(R1) / 1e9:.1f} GOP in {dt1:.2f} s)"}
+    return base, out
+
+
+def parity_against_oracle(torch, B, out, xq1, sx1, y1, xq2, sx2, y2, wh, swh, sh, cand_d):
+    """The GPU's outputs of the rows the CPU baseline computed, bit for bit:
+    quantised activations and scales of both layers, both layers' outputs,
+    and the answer head run on row R-1 of the GPU's down-projection output
+    (candidate logits bit for bit, probabilities within 2^-44)."""
+    R = out["R"]
+    checks = {}
+
+    def cmp_bits(name, got, want):
+        got, want = np.ascontiguousarray(got), np.ascontiguousarray(want)
+        if got.shape != want.shape or got.itemsize != want.itemsize:
+            checks[name] = (int(want.size), int(want.size))
+            return
+        u = {1: np.uint8, 4: np.uint32, 8: np.uint64}[want.itemsize]
+        checks[name] = (int(want.size), int((got.view(u) != want.view(u)).sum()))
+
+    cmp_bits("xq1", xq1[:R].cpu().numpy(), out["xq1"])
+    cmp_bits("sx1", sx1[:R].cpu().numpy(), out["sx1"])
+    cmp_bits("y1", y1[:R].cpu().numpy(), out["y1"])
+    cmp_bits("xq2", xq2[:R].cpu().numpy(), out["xq2"])
+    cmp_bits("sx2", sx2[:R].cpu().numpy(), out["sx2"])
+    cmp_bits("y2", y2[:R].cpu().numpy(), out["y2"])
+    rows = torch.tensor([R - 1], dtype=torch.int32, device="cuda")
+    logits, probs = B.w8a8_answer_head(y2, rows, sh, wh, swh, cand_d)
+    cmp_bits("logits", logits.cpu().numpy(), out["logits"])
+    p = probs.cpu().numpy()
+    bad_p = int((np.abs(p - out["probs"]) > 2.0 ** -44 * np.abs(out["probs"])).sum())
+    checks["probs_within_2^-44"] = (int(p.size), bad_p)
+    return {"checked": sum(c for c, _ in checks.values()), "mismatches": sum(b for _, b in checks.values()),
+            "rows": R, "by_output": {k: {"checked": c, "mismatches": b} for k, (c, b) in checks.items()}}
 
 
 def startup_requantize(torch, B, w1, s1, w2, s2):
@@ -171,7 +237,8 @@ def startup_requantize(torch, B, w1, s1, w2, s2):
 
 def short_request_graph(torch, B, synth):
     """A 256-token request (gate+up, down at split-K 4, answer head over a
-    50000-row lm_head) run eagerly and replayed from one captured HIP graph;
+    50000-row lm_head: 6 launches, the answer head one of them) run eagerly
+    and replayed from one captured HIP graph;
     the answer-head tables stay in device memory, so one capture serves
     every request of the bucket."""
     gu, dn, head = synth.short_request("gate_up"), synth.short_request("down"), synth.lm_head(V=50000)
@@ -238,7 +305,7 @@ def short_request_graph(torch, B, synth):
         out[name] = {"eager_us": round(eager, 1), "graph_us": round(replay, 1),
                      "eager_isolated_us": round(isolated(fn), 1),
                      "graph_isolated_us": round(isolated(g.replay), 1),
-                     "launches": 8 if name == "step" else 3}
+                     "launches": 6 if name == "step" else 1}
     return out
 
 
@@ -281,6 +348,50 @@ def row_parallel_rank(torch, B, x2, s2, w2, sw2, r2):
     return out
 
 
+def roof_us_of(M, N, K, res):
+    """max(ops / int8 MFMA peak, bytes / HBM peak) in microseconds."""
+    ops = 2.0 * M * N * K
+    nbytes = M * K + N * K + 4 * (M + N) + 4 * M * N * (2 if res else 1)
+    return max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+
+
+def large_m_config4(torch, B, synth):
+    """The batch-invariance stress batch (64 requests of U{32..512} tokens in
+    its first arrangement, padded to a multiple of 256) through the
+    5120 -> 15360 layer at split-K 1 and 4: time, TOPS and the fraction of the
+    int8 MFMA peak.  Inputs are the synthetic requests, quantised on the GPU."""
+    reqs, layer = synth.invariance_requests()
+    x, _ = synth.arrangement(reqs, 0)
+    M, K = x.shape
+    N = layer["N"]
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xq, sx = B.w8a8_quantize_act(d(x), d(layer["smooth"]))
+    w, sw = d(layer["w"]), d(layer["sw"])
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    out = {"shape": [int(M), int(N), int(K)], "requests": len(reqs),
+           "tokens": int(sum(r.shape[0] for r in reqs))}
+    ops = 2.0 * M * N * K
+    for S in (1, 4):
+        ws = B.splitk_workspace(M, N, K, S) if S > 1 else None
+        fn = (lambda: B.w8a8_gemm(xq, sx, w, sw, y=y)) if S == 1 else \
+             (lambda: B.w8a8_gemm_splitk(xq, sx, w, sw, S, y=y, workspace=ws))
+        for _ in range(3):
+            fn()
+        t = Timer(torch)
+        for _ in range(10):
+            t.run("g", fn)
+        torch.cuda.synchronize()
+        us = t.mean_us("g")
+        tops = ops / (us * 1e-6) / 1e12
+        out[f"splitk{S}"] = {"us": round(us, 1), "pct_us": t.pct_us("g"), "TOPS": round(tops, 1),
+                             "frac_mfma": round(tops / PEAK_INT8_TOPS, 4),
+                             "plan": B.w8a8_gemm_plan(M, N, K, S, 0)}
+        del ws
+    out["roof_us"] = round(roof_us_of(M, N, K, False), 1)
+    del xq, sx, w, sw, y
+    return out
+
+
 def mid_m_shapes(torch, B, stream_read_gbs):
     """The short-request (M = 256) and forest-batch (M = 328) projections:
     near the ridge of the int8 roofline, so each reports its time against
@@ -320,11 +431,21 @@ def mid_m_shapes(torch, B, stream_read_gbs):
             t.run("g", fn)
         torch.cuda.synchronize()
         us = t.mean_us("g")
+        # the same launches back to back between two events: the time per
+        # layer in a stream of layers (no event between launches)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(30):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us_b2b = 1e3 * e0.elapsed_time(e1) / 30
         ops = 2.0 * M * N * K
         nbytes = M * K + N * K + 4 * (M + N) + 4 * M * N * (2 if res else 1)
         roof_us = max(ops / (PEAK_INT8_TOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
         out[name] = {"shape": [M, N, K], "splitk": S, "plan": B.w8a8_gemm_plan(M, N, K, S, res),
-                     "us": round(us, 1), "pct_us": t.pct_us("g"),
+                     "us": round(us, 1), "pct_us": t.pct_us("g"), "us_back_to_back": round(us_b2b, 1),
+                     "frac_of_roof_back_to_back": round(roof_us_of(M, N, K, res) / us_b2b, 4),
                      "TOPS": round(ops / (us * 1e-6) / 1e12, 1),
                      "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "roof_us": round(roof_us, 1), "frac_of_roof": round(roof_us / us, 4),
@@ -477,6 +598,7 @@ def main():
         q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
 
     mid_m = mid_m_shapes(torch, B, best_read)
+    config4 = large_m_config4(torch, B, synth)
     row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2)
     graph = short_request_graph(torch, B, synth)
     requant = startup_requantize(torch, B, w1, s1, w2, s2)
@@ -498,10 +620,12 @@ def main():
     roofline["sustained_mfma_ceiling_TOPS"] = ceiling["activation_like_16x16x64_TOPS"]
     roofline["frac_of_sustained_ceiling"] = round(gu_tops / ceiling["activation_like_16x16x64_TOPS"], 4)
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(gu, dn, head, cand1, args.cpu_seconds)
+        print("# cpu baseline (oracle) and parity of the same rows", file=sys.stderr, flush=True)
+        cpu, out = cpu_baseline(gu, dn, head, cand1, args.cpu_seconds)
+        parity = parity_against_oracle(torch, B, out, xq1, sx1, y1, xq2, sx2, y2, wh, swh, sh, cand_d)
+        del out
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -511,9 +635,10 @@ def main():
         "config": {"workload": "long-evidence prefill", "M": M, "hidden": K1, "gate_up": N1,
                    "intermediate": K2, "down": N2, "splitk_down": S, "lm_head_rows": head["N"],
                    "candidates": int(cand1.shape[1]), "answer_rows": 1},
-        "roofline": roofline, "cpu_baseline": cpu, "readout": readout, "down": down,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity, "readout": readout, "down": down,
         "quantize": quant, "down_splitk_us": split_us, "kernels_us": kernels,
         "kernels_us_pct": kernels_pct, "mfma_ceiling": ceiling, "mid_m": mid_m,
+        "large_m_config4": config4,
         "row_parallel_rank": row_parallel, "short_request_graph": graph,
         "startup_requantize_q8_0": requant,
     }

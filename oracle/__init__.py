@@ -64,6 +64,8 @@ def load(path: str) -> ctypes.CDLL:
     L.oracle_quantize_act_amax.argtypes = [p, i64, p, p, p, i64, i64, p, p]
     L.oracle_epilogue_acc.argtypes = [p, p, p, p, p, i64, i64]
     L.oracle_requantize_q8_0.argtypes = [p, p, p, i64, i64, p, p]
+    L.oracle_set_num_threads.argtypes = [i32]
+    L.oracle_set_num_threads.restype = None
     for f in ("oracle_quantize_act", "oracle_gemm", "oracle_gemm_sampled", "oracle_gemm_acc",
               "oracle_readout_candidates", "oracle_num_threads", "oracle_row_absmax",
               "oracle_quantize_act_amax", "oracle_epilogue_acc", "oracle_requantize_q8_0"):
@@ -92,6 +94,12 @@ def swap_library(L):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of later calls (each output is computed by one thread
+    in a fixed order, so this never changes a bit)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _ptr(a):

@@ -99,6 +99,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (the results never depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Per-token quantisation after the SmoothQuant per-channel divide.
  *   x        fp32, row r starts at x + r*ldx
  *   row_idx  optional [M]: output row m reads input row row_idx[m]
