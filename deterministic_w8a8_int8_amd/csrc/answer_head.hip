@@ -56,6 +56,7 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
     const int id_raw = lane < C ? cand[m * C + lane] : 0;
     const bool id_ok = id_raw >= 0 && id_raw < V;
     const int id_lane = id_ok ? id_raw : 0;
+    const float sw_lane = lane < C ? sw[id_lane] : 0.0f;   // the candidate's channel scale, requested early
 
     // weight words of the candidates of group g: thread t's word j = t + T*i
     // of row id holds the int8 weights of columns 4j .. 4j+3
@@ -78,22 +79,25 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
     int64_t src;
     const bool ok = source_row(rows, m, h_rows, &src);
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
-    float4 rv[NV];
+    float4 rv[NV], sk[NV];
     bool odd_t;
-    row_reciprocals<NV, T>(s4, K4, rv, odd_t);
+    row_reciprocals<NV, T, true>(s4, K4, rv, odd_t, sk);   // smoothing values kept: no reload on the exact paths
     float4 xv[NV];
     load_row<NV, T>(reinterpret_cast<const float4*>(h + src * ldh), K4, xv);
     uint32_t q[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) q[i] = 0u;
+    uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
     bool valid;
-    const float scale = quantize_row_regs<NV, T, false>(xv, rv, odd_t, s4, K4, ok, 0.0f, red, q, valid);
+    const float scale = quantize_row_regs<NV, T, false, true>(
+        xv, rv, sk, odd_t, s4, K4, ok, 0.0f, red,
+        [&](int i, uint32_t packed) __attribute__((always_inline)) {
+            q[i] = packed;   // kept for the candidate dot products
+            qr[t + i * T] = packed;
+        },
+        valid);
     const float sxm = valid ? scale : quiet_nan();
     if (t == 0) sx[m] = sxm;
-    uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int j = t + i * T;
-        if (j < K4) qr[j] = q[i];
-    }
 
     // candidate logits, AH_GROUP at a time
     for (int g0 = 0, gi = 0; g0 < C; g0 += AH_GROUP, ++gi) {
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
         // lane l < AH_GROUP of wave 0 finishes candidate g0 + l: its id and
         // validity, shuffled from lane g0 + l while every lane is active
         const int src_lane = min(g0 + (lane & (AH_GROUP - 1)), 63);
-        const int id = __shfl(id_lane, src_lane, 64);
+        const float swc = __shfl(sw_lane, src_lane, 64);
         const bool okc = __shfl(static_cast<int>(id_ok), src_lane, 64) != 0;
         __syncthreads();
         if (wave == 0 && lane < AH_GROUP && g0 + lane < C) {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
 #pragma unroll
             for (int v = 0; v < NW; ++v) acc += part[gi & 1][lane][v];
             const int c = g0 + lane;
-            const float l = okc ? scale_acc(acc, sxm, sw[id]) : quiet_nan();
+            const float l = okc ? scale_acc(acc, sxm, swc) : quiet_nan();
             lg[c] = l;
             logits[m * C + c] = l;
             if (!okc && err_flag) atomicOr(err_flag, 1);

@@ -53,11 +53,21 @@ namespace {
 
 constexpr int QTHREADS = 256;   // workgroup of the exact two-pass kernel
 
+// Waves per SIMD the register budget is held to (the second launch bound
+// is a waves-per-execution-unit minimum): the more rows in flight, the closer
+// the scan gets to HBM bandwidth.  8 up to 4 float4 per thread, then 7, 5,
+// 4, 3 and 2 as NV grows -- the most each size reaches without spilling.
+// A 512-thread workgroup puts two waves on each SIMD, so its target is even.
+constexpr int quant_waves_per_simd(int NV, int T) {
+    const int w = NV <= 4 ? 8 : NV == 5 ? 7 : NV == 6 ? 5 : NV <= 9 ? 4 : NV <= 12 ? 3 : 2;
+    return T == 512 ? (w & ~1) : w;
+}
+
 // NV float4 per thread held in registers: K <= NV * 4 * T; ROWS rows per
 // workgroup of T threads.  GIVEN: the per-token maximum comes from amax_in
 // (a row-parallel layer's global maximum) instead of the row itself.
 template <int NV, int T, int ROWS, bool GIVEN>
-__global__ __launch_bounds__(T) void quantize_rows_reg(
+__global__ __launch_bounds__(T, quant_waves_per_simd(NV, T)) void quantize_rows_reg(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
     float* __restrict__ sx, const float* __restrict__ amax_in) {
@@ -69,7 +79,7 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
 
     float4 rv[NV];
     bool odd_t;
-    row_reciprocals<NV, T>(s4, K4, rv, odd_t);
+    row_reciprocals<NV, T>(s4, K4, rv, odd_t, rv);   // smoothing values not kept
 
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
     for (int rr = 0; rr < ROWS; ++rr) {
@@ -79,17 +89,12 @@ __global__ __launch_bounds__(T) void quantize_rows_reg(
         const bool ok = source_row(row_idx, m, x_rows, &src);
         float4 xv[NV];
         load_row<NV, T>(reinterpret_cast<const float4*>(x + src * ldx), K4, xv);
-        uint32_t q[NV];
-        bool valid;
-        const float scale = quantize_row_regs<NV, T, GIVEN>(xv, rv, odd_t, s4, K4, ok,
-                                                            GIVEN ? amax_in[m] : 0.0f, redf[rr & 1], q, valid);
-        if (t == 0) sx[m] = valid ? scale : quiet_nan();
         uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int j = t + i * T;
-            if (j < K4) qr[j] = q[i];
-        }
+        bool valid;
+        const float scale = quantize_row_regs<NV, T, GIVEN, false>(
+            xv, rv, rv, odd_t, s4, K4, ok, GIVEN ? amax_in[m] : 0.0f, redf[rr & 1],
+            [&](int i, uint32_t packed) __attribute__((always_inline)) { qr[t + i * T] = packed; }, valid);
+        if (t == 0) sx[m] = valid ? scale : quiet_nan();
     }
 }
 

@@ -45,6 +45,14 @@ __device__ __forceinline__ int8_t quantize_fast(float x, float r, const float4* 
     return to_code(q);
 }
 
+// The same with the smoothing value at hand (held in a register).
+__device__ __forceinline__ int8_t quantize_fast_s(float x, float r, float s, float scale, float inv) {
+    const float t = (x * r) * inv;
+    const float d = fabsf((t - floorf(t)) - 0.5f);
+    const float q = d > 0x1p-12f ? rintf(t) : rintf((x / s) / scale);
+    return to_code(q);
+}
+
 __device__ __forceinline__ float4 f4(float v) { return make_float4(v, v, v, v); }
 
 __device__ __forceinline__ float absmax4(float m, float4 v) {
@@ -102,15 +110,18 @@ __device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d
 
 // Reciprocals of the smoothing values of the columns a thread holds (float4
 // number t + T*i of the row), and whether any of them lies outside
-// [2^-120, 2^120] (then that thread takes the exact divisions).
-template <int NV, int T>
-__device__ __forceinline__ void row_reciprocals(const float4* s4, int K4, float4 (&rv)[NV], bool& odd_t) {
+// [2^-120, 2^120] (then that thread takes the exact divisions).  With KEEP
+// the smoothing values themselves are kept in keep[] too.
+template <int NV, int T, bool KEEP = false>
+__device__ __forceinline__ void row_reciprocals(const float4* s4, int K4, float4 (&rv)[NV], bool& odd_t,
+                                                float4 (&keep)[NV]) {
     const int t = threadIdx.x;
     odd_t = false;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int j = t + i * T;
         const float4 sv = j < K4 ? s4[j] : f4(1.0f);
+        if constexpr (KEEP) keep[i] = sv;
         rv[i] = make_float4(fast_rcp(sv.x), fast_rcp(sv.y), fast_rcp(sv.z), fast_rcp(sv.w));
         const float lo = fminf(fminf(sv.x, sv.y), fminf(sv.z, sv.w));
         const float hi = fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w));
@@ -129,15 +140,24 @@ __device__ __forceinline__ void load_row(const float4* xr, int K4, float4 (&xv)[
 }
 
 // Quantise one row held in registers (xv, as load_row leaves it): the codes
-// of float4 number t + T*i go to q[i] (four int8 packed little-endian).
+// of float4 number t + T*i (four int8 packed little-endian) are handed to
+// emit(i, packed) as soon as they are computed (i < NV with t + T*i < K/4),
+// so the caller decides whether they are stored at once or kept.
 // Returns the token scale fl(amax/127) (0 for an invalid row) and sets valid
 // (false for a bad row index, ok == false, or a row without a finite
 // maximum).  GIVEN: the maximum is amax_given instead of the row's own.
-// One barrier (the block-wide maximum through red[NW]).
-template <int NV, int T, bool GIVEN>
-__device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const float4 (&rv)[NV], bool odd_t,
-                                                   const float4* s4, int K4, bool ok, float amax_given,
-                                                   float* red, uint32_t (&q)[NV], bool& valid) {
+// With KEEP the rare exact divisions read the smoothing values from sk
+// (kept in registers by row_reciprocals), else from memory (s4): the same
+// values either way.  One barrier (the block-wide maximum through red[NW]).
+template <int NV, int T, bool GIVEN, bool KEEP, class Emit>
+__device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const float4 (&rv)[NV],
+                                                   const float4 (&sk)[NV], bool odd_t, const float4* s4,
+                                                   int K4, bool ok, float amax_given, float* red, Emit&& emit,
+                                                   bool& valid) {
+    auto smooth4 = [&](int i, int j) __attribute__((always_inline)) {
+        if constexpr (KEEP) return sk[i];
+        else return s4[j];
+    };
     constexpr int NW = T / 64;
     const int t = threadIdx.x;
     float amax_loc = 0.0f;   // this thread's approximate maximum
@@ -183,7 +203,7 @@ __device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const
 #pragma unroll
             for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
             if (any) {
-                const float4 sv = s4[j];
+                const float4 sv = smooth4(i, j);
                 const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -201,12 +221,18 @@ __device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int j = t + i * T;
+        if (j >= K4) continue;
         uint32_t packed = 0;
-        if (j < K4 && scale != 0.0f) {
+        if (scale != 0.0f) {
             if (exact) {
-                const float4 sv = s4[j];
+                const float4 sv = smooth4(i, j);
                 packed = pack4(quantize_exact(xv[i].x, sv.x, scale), quantize_exact(xv[i].y, sv.y, scale),
                                quantize_exact(xv[i].z, sv.z, scale), quantize_exact(xv[i].w, sv.w, scale));
+            } else if constexpr (KEEP) {
+                packed = pack4(quantize_fast_s(xv[i].x, rv[i].x, sk[i].x, scale, inv),
+                               quantize_fast_s(xv[i].y, rv[i].y, sk[i].y, scale, inv),
+                               quantize_fast_s(xv[i].z, rv[i].z, sk[i].z, scale, inv),
+                               quantize_fast_s(xv[i].w, rv[i].w, sk[i].w, scale, inv));
             } else {
                 packed = pack4(quantize_fast(xv[i].x, rv[i].x, s4, j, 0, scale, inv),
                                quantize_fast(xv[i].y, rv[i].y, s4, j, 1, scale, inv),
@@ -214,7 +240,7 @@ __device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const
                                quantize_fast(xv[i].w, rv[i].w, s4, j, 3, scale, inv));
             }
         }
-        q[i] = packed;
+        emit(i, packed);
     }
     return scale;
 }
