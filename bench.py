@@ -29,9 +29,14 @@ for bit (the answer head is run once more on row R-1 for it).
 ``large_m_config4`` times the batch-invariance stress batch (64 requests,
 M = 17664 with padding) through 5120 -> 15360 at split-K 1 and 4.
 ``mid_m`` reports each mid-sized projection both with events around every
-launch and as 30 launches back to back.
+launch and as 30 launches back to back.  ``readout.answer_head_us`` is the
+answer head with events around each launch of the step;
+``answer_head_us_back_to_back`` is its device time per launch with 50
+launches queued behind three GEMMs (two events around the 50), and
+``answer_head_host_us_per_call`` the host time the binding takes per call.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--splitk S]
+                       [--legs all|none|splitk,readout,...]
 """
 from __future__ import annotations
 
@@ -85,6 +90,10 @@ def parse():
     ap.add_argument("--M", type=int, default=8192, help="prefill tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--legs", default="all",
+                    help="comma list of the legs run after the timed steps: splitk, readout, stream, mid_m, "
+                         "config4, row_parallel, graph, requant, ceiling, cpu; 'all' (default) or 'none' "
+                         "(shorter runs under a profiler)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -528,6 +537,28 @@ def main():
     value = ops_step / (wall / args.steps) / 1e12
     kernels = {k: round(timer.mean_us(k), 2) for k in timer.pairs}
     kernels_pct = {k: timer.pct_us(k) for k in timer.pairs}
+    legs = set(("splitk,readout,stream,mid_m,config4,row_parallel,graph,requant,ceiling,cpu"
+                if args.legs == "all" else "" if args.legs == "none" else args.legs).split(","))
+
+    # the answer head back to back: 50 launches queued behind three gate+up
+    # GEMMs (about 3.4 ms of device work, longer than the host takes to
+    # enqueue the 50), so the device runs them one after another without
+    # waiting for the host; the host's own time per call is reported too
+    head_fn = lambda: B.w8a8_answer_head(y2, answer, sh, wh, swh, cand_d, xq=xq3, sx=sx3,
+                                         logits=logits, probs=probs)
+    head_b2b, head_host = [], []
+    for _ in range(3):
+        for _ in range(3):
+            B.w8a8_gemm(xq1, sx1, w1, sw1, y=y1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        h0 = time.perf_counter()
+        for _ in range(50):
+            head_fn()
+        head_host.append(1e6 * (time.perf_counter() - h0) / 50)
+        e1.record()
+        torch.cuda.synchronize()
+        head_b2b.append(1e3 * e0.elapsed_time(e1) / 50)
 
     # dominant kernel roofline: gate+up GEMM on the int8 MFMA peak
     gu_us = timer.mean_us("gemm_gate_up")
@@ -549,7 +580,7 @@ def main():
 
     # down projection at other split-K factors (bit-identical output; timed only)
     split_us = {}
-    for s_ in (1, 2, 4, 8):
+    for s_ in ((1, 2, 4, 8) if "splitk" in legs else ()):
         w_ = B.splitk_workspace(M, N2, K2, s_) if s_ > 1 else None
         fn = (lambda: B.w8a8_gemm(xq2, sx2, w2, sw2, residual=r2, y=y2)) if s_ == 1 else \
              (lambda: B.w8a8_gemm_splitk(xq2, sx2, w2, sw2, s_, residual=r2, y=y2, workspace=w_))
@@ -562,66 +593,74 @@ def main():
         split_us[str(s_)] = round(t.mean_us("d"), 1)
         del w_
 
-    # full-vocabulary read-out (M = 3 answer rows): HBM-bound skinny GEMM
-    Mr = rd["answer_rows"].size
-    xqr, sxr = B.w8a8_quantize_act(dev(rd["h"]), sh, row_idx=dev(rd["answer_rows"]))
-    yfull = torch.empty((Mr, head["N"]), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull)
-    t = Timer(torch)
-    for _ in range(20):
-        t.run("full", lambda: B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull))
-    torch.cuda.synchronize()
-    full_us = t.mean_us("full")
-    full_bytes = head["N"] * head["K"] + 4 * head["N"] + Mr * head["K"] + 4 * Mr + 4 * Mr * head["N"]
-    full_gbs = full_bytes / (full_us * 1e-6) / 1e9
-    readout = {"bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-               "frac": round(full_gbs / PEAK_HBM_GBS, 4), "us": round(full_us, 1),
-               "shape": [int(Mr), head["N"], head["K"]], "kernel": "gemm_skinny",
-               "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
-               "answer_head_us": kernels.get("answer_head")}
-
-    # streaming read of 4 GiB: the read bandwidth HBM sustains on this GPU
-    rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
-    rsink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    B.w8a8_probe_stream_read(rbuf, rsink)
-    best_read = 0.0
-    for _ in range(5):
+    readout = {"answer_head_us": kernels.get("answer_head"),
+               "answer_head_us_back_to_back": round(float(np.median(head_b2b)), 2),
+               "answer_head_host_us_per_call": round(float(np.median(head_host)), 2)}
+    if "readout" in legs:
+        # full-vocabulary read-out (M = 3 answer rows): HBM-bound skinny GEMM
+        Mr = rd["answer_rows"].size
+        xqr, sxr = B.w8a8_quantize_act(dev(rd["h"]), sh, row_idx=dev(rd["answer_rows"]))
+        yfull = torch.empty((Mr, head["N"]), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull)
         t = Timer(torch)
-        nbytes = t.run("r", lambda: B.w8a8_probe_stream_read(rbuf, rsink))
+        for _ in range(20):
+            t.run("full", lambda: B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull))
         torch.cuda.synchronize()
-        best_read = max(best_read, nbytes / (t.mean_us("r") * 1e-6) / 1e9)
-    del rbuf
-    readout["stream_read_GBs"] = round(best_read, 1)
-    readout["frac_of_stream_read"] = round(full_gbs / best_read, 4)
-    for q in quant.values():
-        q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
+        full_us = t.mean_us("full")
+        full_bytes = head["N"] * head["K"] + 4 * head["N"] + Mr * head["K"] + 4 * Mr + 4 * Mr * head["N"]
+        full_gbs = full_bytes / (full_us * 1e-6) / 1e9
+        readout = {"bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(full_gbs / PEAK_HBM_GBS, 4), "us": round(full_us, 1),
+                   "shape": [int(Mr), head["N"], head["K"]], "kernel": "gemm_skinny",
+                   "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"), **readout}
+        del yfull
 
-    mid_m = mid_m_shapes(torch, B, best_read)
-    config4 = large_m_config4(torch, B, synth)
-    row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2)
-    graph = short_request_graph(torch, B, synth)
-    requant = startup_requantize(torch, B, w1, s1, w2, s2)
+    best_read = None
+    if "stream" in legs:
+        # streaming read of 4 GiB: the read bandwidth HBM sustains on this GPU
+        rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+        rsink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        B.w8a8_probe_stream_read(rbuf, rsink)
+        best_read = 0.0
+        for _ in range(5):
+            t = Timer(torch)
+            nbytes = t.run("r", lambda: B.w8a8_probe_stream_read(rbuf, rsink))
+            torch.cuda.synchronize()
+            best_read = max(best_read, nbytes / (t.mean_us("r") * 1e-6) / 1e9)
+        del rbuf
+        readout["stream_read_GBs"] = round(best_read, 1)
+        if "achieved" in readout:
+            readout["frac_of_stream_read"] = round(readout["achieved"] / best_read, 4)
+        for q in quant.values():
+            q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
+
+    mid_m = mid_m_shapes(torch, B, best_read) if "mid_m" in legs else None
+    config4 = large_m_config4(torch, B, synth) if "config4" in legs else None
+    row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2) if "row_parallel" in legs else None
+    graph = short_request_graph(torch, B, synth) if "graph" in legs else None
+    requant = startup_requantize(torch, B, w1, s1, w2, s2) if "requant" in legs else None
 
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data and
     # both MFMA forms; the large-M kernel runs 16x16x64
-    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
     ceiling = {}
-    for kind, name in ((0, "uniform_int8"), (1, "activation_like"), (2, "uniform_int8_16x16x64"),
-                       (3, "activation_like_16x16x64")):
-        B.w8a8_probe_mfma_ceiling(kind, 1024, 50, sink)
-        best = 0.0
-        for _ in range(3):
-            t = Timer(torch)
-            ops = t.run("c", lambda: B.w8a8_probe_mfma_ceiling(kind, 1024, 1500, sink))
-            torch.cuda.synchronize()
-            best = max(best, ops / (t.mean_us("c") * 1e-6) / 1e12)
-        ceiling[name + "_TOPS"] = round(best, 1)
-    roofline["sustained_mfma_ceiling_TOPS"] = ceiling["activation_like_16x16x64_TOPS"]
-    roofline["frac_of_sustained_ceiling"] = round(gu_tops / ceiling["activation_like_16x16x64_TOPS"], 4)
+    if "ceiling" in legs:
+        sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+        for kind, name in ((0, "uniform_int8"), (1, "activation_like"), (2, "uniform_int8_16x16x64"),
+                           (3, "activation_like_16x16x64")):
+            B.w8a8_probe_mfma_ceiling(kind, 1024, 50, sink)
+            best = 0.0
+            for _ in range(3):
+                t = Timer(torch)
+                ops = t.run("c", lambda: B.w8a8_probe_mfma_ceiling(kind, 1024, 1500, sink))
+                torch.cuda.synchronize()
+                best = max(best, ops / (t.mean_us("c") * 1e-6) / 1e12)
+            ceiling[name + "_TOPS"] = round(best, 1)
+        roofline["sustained_mfma_ceiling_TOPS"] = ceiling["activation_like_16x16x64_TOPS"]
+        roofline["frac_of_sustained_ceiling"] = round(gu_tops / ceiling["activation_like_16x16x64_TOPS"], 4)
 
     cpu, parity = None, None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and "cpu" in legs:
         print("# cpu baseline (oracle) and parity of the same rows", file=sys.stderr, flush=True)
         cpu, out = cpu_baseline(gu, dn, head, cand1, args.cpu_seconds)
         parity = parity_against_oracle(torch, B, out, xq1, sx1, y1, xq2, sx2, y2, wh, swh, sh, cand_d)

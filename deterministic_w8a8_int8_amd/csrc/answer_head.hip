@@ -12,7 +12,7 @@
 // w8a8_quantize_act (with row_idx), w8a8_readout_candidates and
 // w8a8_candidate_softmax in turn:
 //   - one workgroup per answer row holds the row in registers and quantises
-//     it with quantize_row_regs (the per-token quantisation of quantize.hip);
+//     it with quantize_rows_regs (the per-token quantisation of quantize.hip);
 //   - a candidate logit is the exact int32 dot product of the row's codes
 //     with the candidate's weight row (v_dot4_i32_i8, four int8 products and
 //     an int32 addition, no saturation: K * 127^2 < 2^31 keeps every partial
@@ -75,27 +75,32 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
     };
     if (C > 0) load_group(0);
 
-    // the answer row, quantised (bits of quantize_rows_reg)
+    // the answer row, quantised (bits of quantize_rows_reg); the smoothing
+    // values stay in registers, so no exact path waits on memory
     int64_t src;
-    const bool ok = source_row(rows, m, h_rows, &src);
+    const bool ok1[1] = {source_row(rows, m, h_rows, &src)};
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
-    float4 rv[NV], sk[NV];
+    float4 xv[1][NV];
+    load_row<NV, T>(reinterpret_cast<const float4*>(h + src * ldh), K4, xv[0]);
+    float4 rv[NV], sv[NV];
     bool odd_t;
-    row_reciprocals<NV, T, true>(s4, K4, rv, odd_t, sk);   // smoothing values kept: no reload on the exact paths
-    float4 xv[NV];
-    load_row<NV, T>(reinterpret_cast<const float4*>(h + src * ldh), K4, xv);
+    load_smoothing<NV, T, true>(s4, K4, rv, sv, odd_t);
     uint32_t q[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) q[i] = 0u;
     uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
-    bool valid;
-    const float scale = quantize_row_regs<NV, T, false, true>(
-        xv, rv, sk, odd_t, s4, K4, ok, 0.0f, red,
-        [&](int i, uint32_t packed) __attribute__((always_inline)) {
+    const float no_max[1] = {0.0f};
+    float scale1[1];
+    bool valid1[1];
+    quantize_rows_regs<NV, T, 1, false, true>(
+        xv, rv, sv, odd_t, s4, K4, ok1, no_max, red,
+        [&](int, int i, uint32_t packed) __attribute__((always_inline)) {
             q[i] = packed;   // kept for the candidate dot products
             qr[t + i * T] = packed;
         },
-        valid);
+        scale1, valid1);
+    const float scale = scale1[0];
+    const bool valid = valid1[0];
     const float sxm = valid ? scale : quiet_nan();
     if (t == 0) sx[m] = sxm;
 

@@ -38,6 +38,21 @@ __device__ __forceinline__ float scale_acc_residual(int32_t acc, float sxm, floa
     return y;
 }
 
+// A 16-byte output store, marked non-temporal when `stream_out` (the nt bit:
+// the line is streamed to memory rather than kept).  Outputs much larger
+// than the 256 MB last-level cache are written that way, so that they do not
+// leave it full of dirty lines for the next kernel's reads to wait behind.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_out4(float* p, float4 v, bool stream_out) {
+    if (stream_out)
+        __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
+    else
+        *reinterpret_cast<float4*>(p) = v;
+}
+
+// Outputs of at least this many bytes are stored non-temporally.
+constexpr int64_t STREAM_OUT_BYTES = 64ll << 20;
+
 // Quiet NaN for outputs whose inputs were rejected on the device.
 __device__ __forceinline__ float quiet_nan() { return __builtin_nanf(""); }
 

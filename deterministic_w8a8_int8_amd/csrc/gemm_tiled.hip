@@ -174,7 +174,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, const float* residual, float* y, int M, int N, int K,
     int tiles_m, int tiles_n, int group_m, int splitk, int kb_per_split,
-    int32_t* __restrict__ partials) {
+    int32_t* __restrict__ partials, int stream_out) {
     constexpr int WTM = C::WTM, WTN = C::WTN, BK = C::BK, NST = C::NST;
     __shared__ __attribute__((aligned(1024))) int8_t smem[C::LDS_BYTES + C::PF_BYTES];
 
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                             v.z = scale_acc(a[2], sxm, swv[4 * g + 2]);
                             v.w = scale_acc(a[3], sxm, swv[4 * g + 3]);
                         }
-                        *reinterpret_cast<float4*>(y + o) = v;
+                        store_out4(y + o, v, stream_out);
                     } else {
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                         v.y = scale_acc_residual(a[1], sxm, sw4.y, r4.y);
                         v.z = scale_acc_residual(a[2], sxm, sw4.z, r4.z);
                         v.w = scale_acc_residual(a[3], sxm, sw4.w, r4.w);
-                        *reinterpret_cast<float4*>(y + static_cast<size_t>(row0 + lr) * N + col0 + 4 * c4) = v;
+                        store_out4(y + static_cast<size_t>(row0 + lr) * N + col0 + 4 * c4, v, stream_out);
                         sched_fence();
                     }
                     __syncthreads();
@@ -892,7 +892,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                             v.y = scale_acc_residual(av[k][1], sxv[k], swv[k].y, rv[k].y);
                             v.z = scale_acc_residual(av[k][2], sxv[k], swv[k].z, rv[k].z);
                             v.w = scale_acc_residual(av[k][3], sxv[k], swv[k].w, rv[k].w);
-                            *reinterpret_cast<float4*>(y + ov[k]) = v;
+                            store_out4(y + ov[k], v, stream_out);
                         }
                     } else {
     #pragma unroll
@@ -902,7 +902,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                             v.y = scale_acc(av[k][1], sxv[k], swv[k].y);
                             v.z = scale_acc(av[k][2], sxv[k], swv[k].z);
                             v.w = scale_acc(av[k][3], sxv[k], swv[k].w);
-                            *reinterpret_cast<float4*>(y + ov[k]) = v;
+                            store_out4(y + ov[k], v, stream_out);
                         }
                     }
                     sched_fence();
@@ -938,7 +938,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_tiled(
                         v.z = scale_acc(a4.z, sxm, sw4.z);
                         v.w = scale_acc(a4.w, sxm, sw4.w);
                     }
-                    *reinterpret_cast<float4*>(y + o) = v;
+                    store_out4(y + o, v, stream_out);
                 } else {
                     const int32_t av[4] = {a4.x, a4.y, a4.z, a4.w};
                     const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
@@ -967,7 +967,7 @@ constexpr int REDUCE_THREADS = 256;
 template <bool VEC>
 __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce(
     const int32_t* __restrict__ P, int S, const float* __restrict__ sx,
-    const float* __restrict__ sw, const float* residual, float* y, int64_t M, int64_t N) {
+    const float* __restrict__ sw, const float* residual, float* y, int64_t M, int64_t N, int stream_out) {
     const int64_t MN = M * N;
     const int64_t units = VEC ? MN / 4 : MN;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * REDUCE_THREADS;
@@ -996,7 +996,7 @@ __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce(
                 v.z = scale_acc(a[2], sxm, sw4.z);
                 v.w = scale_acc(a[3], sxm, sw4.w);
             }
-            *reinterpret_cast<float4*>(y + o) = v;
+            store_out4(y + o, v, stream_out);
         } else {
             const int64_t m = u / N;
             const int64_t n = u - m * N;
@@ -1009,6 +1009,8 @@ __global__ __launch_bounds__(REDUCE_THREADS) void splitk_reduce(
 }
 
 }  // namespace
+
+static bool stream_output(const GemmArgs& a) { return a.M * a.N * 4 >= STREAM_OUT_BYTES; }
 
 hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipStream_t stream) {
     const int64_t MN = a.M * a.N;
@@ -1023,11 +1025,11 @@ hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipS
     if (vec)
         hipLaunchKernelGGL((splitk_reduce<true>), dim3(static_cast<unsigned>(blocks)),
                            dim3(REDUCE_THREADS), 0, stream, partials, S, a.sx, a.sw, a.residual,
-                           a.y, a.M, a.N);
+                           a.y, a.M, a.N, static_cast<int>(stream_output(a)));
     else
         hipLaunchKernelGGL((splitk_reduce<false>), dim3(static_cast<unsigned>(blocks)),
                            dim3(REDUCE_THREADS), 0, stream, partials, S, a.sx, a.sw, a.residual,
-                           a.y, a.M, a.N);
+                           a.y, a.M, a.N, static_cast<int>(stream_output(a)));
     return hipGetLastError();
 }
 
@@ -1056,7 +1058,8 @@ hipError_t launch_cfg(const GemmArgs& a, const GemmPlan& p, void* workspace, hip
     hipLaunchKernelGGL((gemm_tiled<C>), dim3(nblocks), dim3(C::THREADS), 0, stream, a.xq, a.sx, a.w,
                        a.sw, a.residual, a.y, static_cast<int>(a.M), static_cast<int>(a.N),
                        static_cast<int>(a.K), static_cast<int>(p.tiles_m),
-                       static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, partials);
+                       static_cast<int>(p.tiles_n), p.group_m, p.splitk, kb_per_split, partials,
+                       static_cast<int>(stream_output(a)));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splitk <= 1 || a.acc_out) return e;
     return launch_reduce(a, p.splitk, partials, stream);

@@ -10,9 +10,10 @@
 //   q  = clamp(rne(fl(x' / sx)), -127, 127), or 0 when sx == 0
 //
 // Design (HBM-bound scan, 4 B read + 1 B written per element):
-//   - a workgroup of T = 256 or 512 threads handles one row; thread t holds
-//     float4 number t + T*i of the row in registers, so each row is read from
-//     HBM once and every wave-level load is 1 KiB contiguous;
+//   - a workgroup of T = 256, 512 or 1024 threads handles one row; thread t
+//     holds float4 number t + T*i of the row in registers, so each row is
+//     read from HBM once (non-temporal loads) and every wave-level load is
+//     1 KiB contiguous;
 //   - exact results without a true division per element.  Two correctly
 //     rounded divisions per element would cost as much as the memory
 //     traffic, so the kernel works with reciprocals and proves, per element,
@@ -23,18 +24,22 @@
 //         only).  Because fl() is monotone, the wave's exact maximum
 //         fl(|x_k|/s_k) is reached by an element whose approximation lies
 //         within 2^-19 of that approximate maximum; only those few
-//         candidates are divided exactly.  One block-wide maximum of the
-//         waves' exact maxima is the row's -- a single barrier per row;
+//         candidates are divided exactly (the test is made once per float4,
+//         on the maximum of its four approximations kept from the first
+//         pass).  One block-wide maximum of the waves' exact maxima is the
+//         row's -- a single barrier per row;
 //       * with sx = fl(a/127) (a true division, once per row) and inv =
 //         rcp(sx), t' = (x*r)*inv is within 2^-14 of t = fl(fl(x/s)/sx)
 //         whenever |t| <= 128.  If t' is more than 2^-12 away from every
 //         half-integer, rne(t') = rne(t).  Otherwise (about 5 in 10^4
-//         elements) both true divisions are done;
+//         elements) both true divisions are done for its float4 (one
+//         branch per float4);
 //       * where subnormal intermediates void the relative error bounds the
 //         exact divisions are used throughout: a thread holding a smoothing
 //         value outside [2^-120, 2^120] (for its elements; its wave divides
 //         every element for the maximum), a wave whose approximate maximum is
-//         below 2^-96 (for its maximum), and a row whose maximum is below
+//         below 2^-96 or at least 2^126 or that holds a non-finite
+//         approximation (for its maximum), and a row whose maximum is below
 //         2^-96 (for every element);
 //   - the row maximum is a wave64 shuffle reduction, then per-wave partial
 //     maxima through LDS (max is exact, so order does not matter);
@@ -53,48 +58,56 @@ namespace {
 
 constexpr int QTHREADS = 256;   // workgroup of the exact two-pass kernel
 
-// Waves per SIMD the register budget is held to (the second launch bound
-// is a waves-per-execution-unit minimum): the more rows in flight, the closer
-// the scan gets to HBM bandwidth.  8 up to 4 float4 per thread, then 7, 5,
-// 4, 3 and 2 as NV grows -- the most each size reaches without spilling.
-// A 512-thread workgroup puts two waves on each SIMD, so its target is even.
-constexpr int quant_waves_per_simd(int NV, int T) {
-    const int w = NV <= 4 ? 8 : NV == 5 ? 7 : NV == 6 ? 5 : NV <= 9 ? 4 : NV <= 12 ? 3 : 2;
-    return T == 512 ? (w & ~1) : w;
-}
-
-// NV float4 per thread held in registers: K <= NV * 4 * T; ROWS rows per
-// workgroup of T threads.  GIVEN: the per-token maximum comes from amax_in
-// (a row-parallel layer's global maximum) instead of the row itself.
-template <int NV, int T, int ROWS, bool GIVEN>
-__global__ __launch_bounds__(T, quant_waves_per_simd(NV, T)) void quantize_rows_reg(
+// NV float4 per thread held in registers: K <= NV * 4 * T; R rows per
+// workgroup of T threads, quantised together (one barrier and one set of
+// reciprocals for the R rows; the library launches R = 1).  GIVEN: the per-token maximum comes from
+// amax_in (a row-parallel layer's global maximum) instead of the row itself.
+// KEEP: the smoothing values stay in registers for the rare exact paths.
+template <int NV, int T, int R, bool GIVEN, bool KEEP, int WAVES>
+__global__ __launch_bounds__(T, WAVES) void quantize_rows_reg(
     const float* __restrict__ x, int64_t ldx, int64_t x_rows, const int32_t* __restrict__ row_idx,
     const float* __restrict__ smooth, int64_t M, int64_t K, int8_t* __restrict__ xq,
     float* __restrict__ sx, const float* __restrict__ amax_in) {
     constexpr int NW = T / 64;
-    __shared__ float redf[2][NW];
+    __shared__ float red[R * NW];
     const float4* s4 = reinterpret_cast<const float4*>(smooth);
     const int K4 = static_cast<int>(K >> 2);
     const int t = threadIdx.x;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * R;
 
-    float4 rv[NV];
+    bool live[R], ok[R];
+    float amax_g[R];
+    float4 xv[R][NV];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t m = m0 + r;
+        live[r] = m < M;
+        int64_t src = 0;
+        ok[r] = live[r] && source_row(row_idx, m, x_rows, &src);
+        amax_g[r] = GIVEN && live[r] ? amax_in[m] : 0.0f;
+        if (live[r]) {
+            load_row<NV, T>(reinterpret_cast<const float4*>(x + src * ldx), K4, xv[r]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) xv[r][i] = f4(0.0f);
+        }
+    }
+    float4 rv[NV], sv[NV];
     bool odd_t;
-    row_reciprocals<NV, T>(s4, K4, rv, odd_t, rv);   // smoothing values not kept
+    load_smoothing<NV, T, KEEP>(s4, K4, rv, sv, odd_t);
 
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
-    for (int rr = 0; rr < ROWS; ++rr) {
-        const int64_t m = m0 + rr;
-        if (m >= M) break;   // uniform across the block
-        int64_t src;
-        const bool ok = source_row(row_idx, m, x_rows, &src);
-        float4 xv[NV];
-        load_row<NV, T>(reinterpret_cast<const float4*>(x + src * ldx), K4, xv);
-        uint32_t* qr = reinterpret_cast<uint32_t*>(xq + m * K);
-        bool valid;
-        const float scale = quantize_row_regs<NV, T, GIVEN, false>(
-            xv, rv, rv, odd_t, s4, K4, ok, GIVEN ? amax_in[m] : 0.0f, redf[rr & 1],
-            [&](int i, uint32_t packed) __attribute__((always_inline)) { qr[t + i * T] = packed; }, valid);
-        if (t == 0) sx[m] = valid ? scale : quiet_nan();
+    float scale[R];
+    bool valid[R];
+    quantize_rows_regs<NV, T, R, GIVEN, KEEP>(
+        xv, rv, sv, odd_t, s4, K4, ok, amax_g, red,
+        [&](int r, int i, uint32_t packed) __attribute__((always_inline)) {
+            if (live[r]) reinterpret_cast<uint32_t*>(xq + (m0 + r) * K)[t + i * T] = packed;
+        },
+        scale, valid);
+    if (t == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (live[r]) sx[m0 + r] = valid[r] ? scale[r] : quiet_nan();
     }
 }
 
@@ -152,18 +165,15 @@ __global__ __launch_bounds__(QTHREADS) void quantize_rows_stream(
     }
 }
 
-template <int NV, int T>
+template <int NV, int T, int R, bool KEEP, int WAVES>
 hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
-    // One row per workgroup: measured faster than sharing the reciprocals
-    // over several rows, because more workgroups keep more rows in flight.
+    const dim3 grid(static_cast<unsigned>((a.M + R - 1) / R));
     if (a.amax)
-        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, true>), dim3(static_cast<unsigned>(a.M)), dim3(T),
-                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
-                           a.amax);
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, R, true, KEEP, WAVES>), grid, dim3(T), 0, stream, a.x, a.ldx,
+                           a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx, a.amax);
     else
-        hipLaunchKernelGGL((quantize_rows_reg<NV, T, 1, false>), dim3(static_cast<unsigned>(a.M)), dim3(T),
-                           0, stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx,
-                           nullptr);
+        hipLaunchKernelGGL((quantize_rows_reg<NV, T, R, false, KEEP, WAVES>), grid, dim3(T), 0, stream, a.x, a.ldx,
+                           a.x_rows, a.row_idx, a.smooth, a.M, a.K, a.xq, a.sx, nullptr);
     return hipGetLastError();
 }
 
@@ -171,21 +181,28 @@ hipError_t launch_reg(const QuantArgs& a, hipStream_t stream) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
-    const int64_t n256 = (a.K + 1023) / 1024;   // float4 per thread with 256 threads
-    const int64_t n512 = (a.K + 2047) / 2048;   // ... with 512 threads
-    if (n256 <= 1) return launch_reg<1, 256>(a, stream);
-    if (n256 <= 2) return launch_reg<2, 256>(a, stream);
-    if (n256 <= 3) return launch_reg<3, 256>(a, stream);
-    if (n256 <= 4) return launch_reg<4, 256>(a, stream);
-    if (n256 <= 5) return launch_reg<5, 256>(a, stream);
-    if (n256 <= 6) return launch_reg<6, 256>(a, stream);
-    if (n512 <= 4) return launch_reg<4, 512>(a, stream);
-    if (n512 <= 5) return launch_reg<5, 512>(a, stream);
-    if (n512 <= 6) return launch_reg<6, 512>(a, stream);
-    if (n512 <= 8) return launch_reg<8, 512>(a, stream);
-    if (n512 <= 9) return launch_reg<9, 512>(a, stream);
-    if (n512 <= 12) return launch_reg<12, 512>(a, stream);
-    if (n512 <= 16) return launch_reg<16, 512>(a, stream);
+    // Threads per row and float4 per thread by K; the second argument of
+    // launch_reg's template is the workgroup size, the last the waves per
+    // SIMD its register budget is held to (the most each reaches without
+    // spilling).  Measured on 8192-row batches: one row per workgroup beats
+    // two (more workgroups, more rows in flight), and 1024 threads beat 512
+    // at K = 17408 (155 against 166 us).
+    const int64_t n256 = (a.K + 1023) / 1024;    // float4 per thread with 256 threads
+    const int64_t n512 = (a.K + 2047) / 2048;    // ... with 512 threads
+    const int64_t n1024 = (a.K + 4095) / 4096;   // ... with 1024 threads
+    if (n256 <= 1) return launch_reg<1, 256, 1, false, 8>(a, stream);
+    if (n256 <= 2) return launch_reg<2, 256, 1, false, 8>(a, stream);
+    if (n256 <= 3) return launch_reg<3, 256, 1, false, 8>(a, stream);
+    if (n256 <= 4) return launch_reg<4, 256, 1, false, 8>(a, stream);
+    if (n256 <= 5) return launch_reg<5, 256, 1, false, 7>(a, stream);
+    if (n256 <= 6) return launch_reg<6, 256, 1, false, 6>(a, stream);
+    if (n512 <= 4) return launch_reg<4, 512, 1, false, 8>(a, stream);
+    if (n512 <= 5) return launch_reg<5, 512, 1, false, 6>(a, stream);
+    if (n512 <= 6) return launch_reg<6, 512, 1, false, 6>(a, stream);
+    if (n512 <= 8) return launch_reg<8, 512, 1, false, 4>(a, stream);
+    if (n1024 <= 5) return launch_reg<5, 1024, 1, false, 8>(a, stream);
+    if (n512 <= 12) return launch_reg<12, 512, 1, false, 2>(a, stream);
+    if (n512 <= 16) return launch_reg<16, 512, 1, false, 2>(a, stream);
     hipLaunchKernelGGL(quantize_rows_stream, dim3(static_cast<unsigned>(a.M)), dim3(QTHREADS), 0,
                        stream, a.x, a.ldx, a.x_rows, a.row_idx, a.smooth, a.K, a.xq, a.sx, a.amax);
     return hipGetLastError();

@@ -29,35 +29,7 @@ __device__ __forceinline__ int8_t quantize_exact(float x, float s, float scale) 
     return to_code(rintf(t));
 }
 
-// Fast quantisation with the proof described above; falls back to the exact
-// divisions when the approximate quotient is near a rounding boundary.
-__device__ __forceinline__ int8_t quantize_fast(float x, float r, const float4* s4, int j, int c,
-                                                float scale, float inv) {
-    const float t = (x * r) * inv;
-    const float d = fabsf((t - floorf(t)) - 0.5f);
-    float q;
-    if (d > 0x1p-12f) {
-        q = rintf(t);
-    } else {
-        const float s = reinterpret_cast<const float*>(s4)[4 * j + c];
-        q = rintf((x / s) / scale);
-    }
-    return to_code(q);
-}
-
-// The same with the smoothing value at hand (held in a register).
-__device__ __forceinline__ int8_t quantize_fast_s(float x, float r, float s, float scale, float inv) {
-    const float t = (x * r) * inv;
-    const float d = fabsf((t - floorf(t)) - 0.5f);
-    const float q = d > 0x1p-12f ? rintf(t) : rintf((x / s) / scale);
-    return to_code(q);
-}
-
 __device__ __forceinline__ float4 f4(float v) { return make_float4(v, v, v, v); }
-
-__device__ __forceinline__ float absmax4(float m, float4 v) {
-    return fmaxf(fmaxf(fmaxf(m, fabsf(v.x)), fmaxf(fabsf(v.y), fabsf(v.z))), fabsf(v.w));
-}
 
 // |v| for the exact row maximum, with NaN mapped to +Inf: a row holding a
 // NaN or infinite smoothed value then has an infinite maximum (fmaxf alone
@@ -108,141 +80,197 @@ __device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d
            (static_cast<uint32_t>(static_cast<uint8_t>(d)) << 24);
 }
 
-// Reciprocals of the smoothing values of the columns a thread holds (float4
-// number t + T*i of the row), and whether any of them lies outside
-// [2^-120, 2^120] (then that thread takes the exact divisions).  With KEEP
-// the smoothing values themselves are kept in keep[] too.
-template <int NV, int T, bool KEEP = false>
-__device__ __forceinline__ void row_reciprocals(const float4* s4, int K4, float4 (&rv)[NV], bool& odd_t,
-                                                float4 (&keep)[NV]) {
+// The smoothing values of the columns a thread holds (float4 number t + T*i
+// of a row; 1 past K), their reciprocals r = rcp(s) (|error| <= 1 ulp), and
+// whether any of them lies outside [2^-120, 2^120] (then that thread takes
+// the exact divisions).  With KEEP the smoothing values stay in registers
+// (sv) for the exact paths; otherwise those paths read them from memory.
+template <int NV, int T, bool KEEP>
+__device__ __forceinline__ void load_smoothing(const float4* s4, int K4, float4 (&rv)[NV], float4 (&sv)[NV],
+                                               bool& odd_t) {
     const int t = threadIdx.x;
     odd_t = false;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int j = t + i * T;
-        const float4 sv = j < K4 ? s4[j] : f4(1.0f);
-        if constexpr (KEEP) keep[i] = sv;
-        rv[i] = make_float4(fast_rcp(sv.x), fast_rcp(sv.y), fast_rcp(sv.z), fast_rcp(sv.w));
-        const float lo = fminf(fminf(sv.x, sv.y), fminf(sv.z, sv.w));
-        const float hi = fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w));
+        const float4 v = j < K4 ? s4[j] : f4(1.0f);
+        if constexpr (KEEP) sv[i] = v;
+        rv[i] = make_float4(fast_rcp(v.x), fast_rcp(v.y), fast_rcp(v.z), fast_rcp(v.w));
+        const float lo = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
+        const float hi = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
         odd_t |= !(lo >= 0x1p-120f && hi <= 0x1p120f);
     }
 }
 
-// Thread t's float4 numbers t + T*i of a row (zeros past K).
+// Thread t's float4 numbers t + T*i of a row (zeros past K).  The loads are
+// non-temporal: each row is read once, and streaming it past the caches
+// measured 3% faster on 8192 x 17408 batches.
 template <int NV, int T>
 __device__ __forceinline__ void load_row(const float4* xr, int K4, float4 (&xv)[NV]) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int j = threadIdx.x + i * T;
-        xv[i] = j < K4 ? xr[j] : f4(0.0f);
+        if (j < K4) {
+            const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(xr + j));
+            xv[i] = make_float4(v.x, v.y, v.z, v.w);
+        } else {
+            xv[i] = f4(0.0f);
+        }
     }
 }
 
-// Quantise one row held in registers (xv, as load_row leaves it): the codes
-// of float4 number t + T*i (four int8 packed little-endian) are handed to
-// emit(i, packed) as soon as they are computed (i < NV with t + T*i < K/4),
-// so the caller decides whether they are stored at once or kept.
-// Returns the token scale fl(amax/127) (0 for an invalid row) and sets valid
-// (false for a bad row index, ok == false, or a row without a finite
-// maximum).  GIVEN: the maximum is amax_given instead of the row's own.
-// With KEEP the rare exact divisions read the smoothing values from sk
-// (kept in registers by row_reciprocals), else from memory (s4): the same
-// values either way.  One barrier (the block-wide maximum through red[NW]).
-template <int NV, int T, bool GIVEN, bool KEEP, class Emit>
-__device__ __forceinline__ float quantize_row_regs(const float4 (&xv)[NV], const float4 (&rv)[NV],
-                                                   const float4 (&sk)[NV], bool odd_t, const float4* s4,
-                                                   int K4, bool ok, float amax_given, float* red, Emit&& emit,
-                                                   bool& valid) {
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) {
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+__device__ __forceinline__ float max4abs(float4 a) {
+    return fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+}
+
+// The fast code of one element: t' = (x*r)*inv rounded to nearest even and
+// clamped.  near is set when t' lies within 2^-12 of a half-integer (or is
+// not finite): |t' - rint(t')| is exact (Sterbenz, or rint(t') = 0), and it
+// exceeds 1/2 - 2^-12 exactly when t' is that close to k + 1/2.  Only then
+// can rne(t') differ from rne(fl(fl(x/s)/sx)).
+__device__ __forceinline__ int fast_code(float x, float r, float inv, bool& near) {
+    const float t = (x * r) * inv;
+    const float q = rintf(t);
+    near |= !(fabsf(t - q) < 0.5f - 0x1p-12f);
+    return static_cast<int>(fminf(fmaxf(q, -127.0f), 127.0f));
+}
+
+__device__ __forceinline__ uint32_t pack4i(int a, int b, int c, int d) {
+    return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
+           ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
+}
+
+// Quantise R rows held in registers at once (xv[r], as load_row leaves them;
+// rv, sv and odd_t as load_smoothing leaves them).  The codes of float4
+// number t + T*i of row r (four int8 packed little-endian) are handed to
+// emit(r, i, packed) as soon as they are final (for t + T*i < K/4), so the
+// caller decides whether they are stored at once or kept.  scale[r] is the
+// token scale fl(amax/127) (0 for an invalid row); valid[r] is false for
+// ok[r] == false or a row without a finite maximum.  GIVEN: the maximum is
+// amax_given[r] instead of the row's own.  One barrier for all R rows (the
+// block-wide maxima through red[R * NW]).
+//
+// The work per element is kept small, since at HBM speed the scan has few
+// vector-ALU cycles to spare per element: the first pass keeps each float4's
+// approximate maximum magnitude (m4), so the second pass tests one value per
+// float4 for being a maximum candidate; non-finite smoothed values are found
+// from a running sum of the approximations (a NaN or infinity propagates; an
+// overflow of the sum only sends the wave down the exact path); and the code
+// pass takes one branch per float4, to the exact divisions, when any of its
+// four values lies near a rounding boundary.
+template <int NV, int T, int R, bool GIVEN, bool KEEP, class Emit>
+__device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], const float4 (&rv)[NV],
+                                                   const float4 (&sv)[NV], bool odd_t, const float4* s4, int K4,
+                                                   const bool (&ok)[R], const float (&amax_given)[R], float* red,
+                                                   Emit&& emit, float (&scale)[R], bool (&valid)[R]) {
     auto smooth4 = [&](int i, int j) __attribute__((always_inline)) {
-        if constexpr (KEEP) return sk[i];
+        if constexpr (KEEP) return sv[i];
         else return s4[j];
     };
     constexpr int NW = T / 64;
     const int t = threadIdx.x;
-    float amax_loc = 0.0f;   // this thread's approximate maximum
-    bool huge_t = false;     // an approximation that is NaN, infinite or >= 2^126
-    if constexpr (!GIVEN) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const float4 ap = make_float4(xv[i].x * rv[i].x, xv[i].y * rv[i].y,
-                                          xv[i].z * rv[i].z, xv[i].w * rv[i].w);
-            amax_loc = absmax4(amax_loc, ap);
-            huge_t |= !(fabsf(ap.x) < 0x1p126f) || !(fabsf(ap.y) < 0x1p126f) ||
-                      !(fabsf(ap.z) < 0x1p126f) || !(fabsf(ap.w) < 0x1p126f);
-        }
-    }
-    float amax = 0.0f;
+    float amax[R];
     if constexpr (GIVEN) {
         // a given maximum: no reduction over the row.  A NaN, negative or
         // infinite one marks the row invalid, like a bad row index.
-        amax = amax_given;
-        valid = ok && usable_max(amax);
+#pragma unroll
+        for (int r = 0; r < R; ++r) amax[r] = amax_given[r];
     } else {
+        float m4[R][NV];       // per float4: max |x * r| over its four values
+        float amax_loc[R], fin[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            amax_loc[r] = 0.0f;
+            fin[r] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const float4 ap = mul4(xv[r][i], rv[i]);
+                m4[r][i] = max4abs(ap);
+                amax_loc[r] = fmaxf(amax_loc[r], m4[r][i]);
+                fin[r] += (ap.x + ap.y) + (ap.z + ap.w);
+            }
+        }
         // This wave's exact maximum: the element holding it has an
-        // approximation within 2^-21 of the wave's approximate maximum
-        // (a shuffle reduction, no barrier), so only elements within
-        // 2^-19 of it -- usually one per wave -- are divided exactly; all
-        // of the wave's are when the approximations cannot be trusted
-        // (an odd smoothing value in the wave, a maximum below 2^-96, or
-        // an approximation that is NaN, infinite or near overflow, where
-        // fl(x/s) may overflow while x*rcp(s) does not or the reverse).
-        // One block-wide maximum of the exact values gives the row's; a
+        // approximation within 2^-21 of the wave's approximate maximum (a
+        // shuffle reduction, no barrier), so only elements within 2^-19 of
+        // it -- usually one per wave -- are divided exactly; all of the
+        // wave's are when the approximations cannot be trusted (an odd
+        // smoothing value in the wave, a maximum below 2^-96 or at least
+        // 2^126, or a NaN or infinity among the approximations, where
+        // fl(x/s) may overflow while x*rcp(s) does not or the reverse).  One
+        // block-wide maximum of the exact values gives the row's; a
         // non-finite smoothed value makes it +Inf.
-        const float amax_w = wave_max(amax_loc);
-        const bool all_exact = __any(odd_t) || __any(huge_t) || !(amax_w >= 0x1p-96f);
-        const float thresh = amax_w * (1.0f - 0x1p-19f);
-        float amax_t = 0.0f;
+        float amax_t[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float amax_w = wave_max(amax_loc[r]);
+            const bool all_exact = __any(odd_t || !(fin[r] - fin[r] == 0.0f)) ||
+                                   !(amax_w >= 0x1p-96f && amax_w < 0x1p126f);
+            const float thresh = amax_w * (1.0f - 0x1p-19f);
+            amax_t[r] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int j = t + i * T;
+                if (j < K4 && (all_exact || m4[r][i] >= thresh)) {
+                    const float4 ap = mul4(xv[r][i], rv[i]);
+                    const float4 sv4 = smooth4(i, j);
+                    const float xs[4] = {xv[r][i].x, xv[r][i].y, xv[r][i].z, xv[r][i].w};
+                    const float as[4] = {ap.x, ap.y, ap.z, ap.w};
+                    const float ss[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (all_exact || fabsf(as[c]) >= thresh) amax_t[r] = fmaxf(amax_t[r], abs_nf(xs[c] / ss[c]));
+                }
+            }
+            amax_t[r] = wave_max(amax_t[r]);
+        }
+        const int wave = t >> 6;
+        if ((t & 63) == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) red[r * NW + wave] = amax_t[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            amax[r] = red[r * NW];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) amax[r] = fmaxf(amax[r], red[r * NW + w]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        valid[r] = ok[r] && usable_max(amax[r]);
+        // tiny rows (or odd smoothing values) take the exact divisions
+        const bool exact = odd_t || !(amax[r] >= 0x1p-96f);
+        const float sc = valid[r] ? amax[r] / 127.0f : 0.0f;
+        scale[r] = sc;
+        const float inv = fast_rcp(sc);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int j = t + i * T;
             if (j >= K4) continue;
-            const float xs[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            const float rs[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
-            bool any = all_exact;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) any |= fabsf(xs[c] * rs[c]) >= thresh;
-            if (any) {
-                const float4 sv = smooth4(i, j);
-                const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (all_exact || fabsf(xs[c] * rs[c]) >= thresh)
-                        amax_t = fmaxf(amax_t, abs_nf(xs[c] / ss[c]));
+            uint32_t packed = 0;
+            if (sc != 0.0f) {
+                const float4 x = xv[r][i];
+                bool near = exact;
+                if (!exact) {
+                    const float4 rr = rv[i];
+                    packed = pack4i(fast_code(x.x, rr.x, inv, near), fast_code(x.y, rr.y, inv, near),
+                                    fast_code(x.z, rr.z, inv, near), fast_code(x.w, rr.w, inv, near));
+                }
+                if (near) {
+                    const float4 v = smooth4(i, j);
+                    packed = pack4(quantize_exact(x.x, v.x, sc), quantize_exact(x.y, v.y, sc),
+                                   quantize_exact(x.z, v.z, sc), quantize_exact(x.w, v.w, sc));
+                }
             }
+            emit(r, i, packed);
         }
-        amax = block_max<NW>(amax_t, red);
-        valid = ok && usable_max(amax);
     }
-    // tiny rows (or odd smoothing values) take the exact divisions
-    const bool exact = odd_t || !(amax >= 0x1p-96f);
-    const float scale = valid ? amax / 127.0f : 0.0f;
-    const float inv = fast_rcp(scale);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int j = t + i * T;
-        if (j >= K4) continue;
-        uint32_t packed = 0;
-        if (scale != 0.0f) {
-            if (exact) {
-                const float4 sv = smooth4(i, j);
-                packed = pack4(quantize_exact(xv[i].x, sv.x, scale), quantize_exact(xv[i].y, sv.y, scale),
-                               quantize_exact(xv[i].z, sv.z, scale), quantize_exact(xv[i].w, sv.w, scale));
-            } else if constexpr (KEEP) {
-                packed = pack4(quantize_fast_s(xv[i].x, rv[i].x, sk[i].x, scale, inv),
-                               quantize_fast_s(xv[i].y, rv[i].y, sk[i].y, scale, inv),
-                               quantize_fast_s(xv[i].z, rv[i].z, sk[i].z, scale, inv),
-                               quantize_fast_s(xv[i].w, rv[i].w, sk[i].w, scale, inv));
-            } else {
-                packed = pack4(quantize_fast(xv[i].x, rv[i].x, s4, j, 0, scale, inv),
-                               quantize_fast(xv[i].y, rv[i].y, s4, j, 1, scale, inv),
-                               quantize_fast(xv[i].z, rv[i].z, s4, j, 2, scale, inv),
-                               quantize_fast(xv[i].w, rv[i].w, s4, j, 3, scale, inv));
-            }
-        }
-        emit(i, packed);
-    }
-    return scale;
 }
 
 }  // namespace w8a8

@@ -187,6 +187,20 @@ def arrangement(reqs, k: int, base: int = 1004, max_pad: int = 15, align: int = 
     return np.concatenate(blocks, axis=0), starts
 
 
+def block_points(rng, M: int, N: int, bm: int, bn: int):
+    """One random output coordinate inside every bm x bn block of an M x N
+    output (the ragged edge blocks included), so that a sampled check touches
+    every tile and every per-wave sub-tile of a blocked kernel."""
+    rb, cb = -(-M // bm), -(-N // bn)
+    r0 = np.repeat(np.arange(rb, dtype=np.int64) * bm, cb)
+    c0 = np.tile(np.arange(cb, dtype=np.int64) * bn, rb)
+    hr = np.minimum(bm, M - r0)
+    hc = np.minimum(bn, N - c0)
+    mi = r0 + (rng.random(r0.size) * hr).astype(np.int64)
+    ni = c0 + (rng.random(c0.size) * hc).astype(np.int64)
+    return mi, ni
+
+
 def sample_points(rng, M: int, N: int, count: int, must_rows=(), must_cols=()):
     """Sampled output coordinates: random ones plus the corners and the given
     rows/columns' first entries, for checking huge outputs one by one."""

@@ -3,8 +3,9 @@
 Each case runs the C-ABI path at full size.  The oracle cannot afford every
 output of these shapes, so the checks are:
 * every quantised activation and token scale, bit for bit;
-* whole output rows and several thousand sampled outputs, bit for bit
-  against the oracle, computed one by one;
+* whole output rows, several thousand random outputs and one output in
+  every 16 x 16 or 32 x 32 output block (so every tile and every wave's
+  sub-tile), bit for bit against the oracle, computed one by one;
 * properties that hold at any size: split-K, batch arrangement, padding and
   forest branches, each bitwise equal to the reference run, and candidate
   logits bitwise equal to the full-vocabulary columns;
@@ -55,6 +56,13 @@ def check_layer(d, *, splits=(1,), rows_full=2, seed=0, label=""):
         del ys
     rng = np.random.default_rng(seed)
     mi, ni = synth.sample_points(rng, M, N, N_SAMPLES)
+    # plus one output in every 16 x 16 block (M <= 512: the skinny and panel
+    # kernels' row groups and 16-column wave strips) or 32 x 32 block (the
+    # tiled kernel's per-wave MFMA tiles), so every tile is touched
+    blk = 16 if M <= 512 else 32
+    bi, bj = synth.block_points(rng, M, N, blk, blk)
+    mi, ni = np.concatenate([mi, bi]), np.concatenate([ni, bj])
+    say(f"{label}: {mi.size} sampled outputs")
     got = host(y1[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()])
     want = oracle.gemm_sampled(xq_o, sx_o, d["w"], d["sw"], mi, ni, residual=d["r"])
     assert_bits_equal(got, want, f"{label} sampled")
