@@ -73,6 +73,15 @@ __device__ __forceinline__ void lds_fill16(const int8_t* gbase, uint32_t voff, l
                  : "memory");
 }
 
+// The same copy with the non-temporal cache policy (nt): for data read once
+// per launch, streamed past the caches.
+__device__ __forceinline__ void lds_fill16_nt(const int8_t* gbase, uint32_t voff, lds_i8* lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(gbase), "{m0}"(lds)
+                 : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }

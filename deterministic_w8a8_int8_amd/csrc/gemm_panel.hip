@@ -57,6 +57,7 @@ constexpr int PANEL_THREADS = 256;  // 4 waves, one per SIMD
 constexpr int KBS = 2;              // 64-byte K-blocks per stage
 constexpr int ROW_BYTES = 64 * KBS; // bytes of one row in a stage (8 chunks of 16)
 constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: raw 32-bit data
+constexpr int kNonTemporal = 2;           // cache-policy operand of a buffer load: the nt bit
 
 struct PanelParams {
     int M, N, K;
@@ -80,7 +81,8 @@ constexpr int ring_size(int g, int want) {
     return g;
 }
 
-template <int MW, int NB, int NSET, int NSLOT>
+// WNT: the weight loads are non-temporal (streamed past the caches).
+template <int MW, int NB, int NSET, int NSLOT, bool WNT>
 __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, const float* residual, float* y, int32_t* __restrict__ partials,
@@ -168,7 +170,10 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
     auto piece_load = [&](i32x4& dst, int st, int q) __attribute__((always_inline)) {
         st = min(st, nst - 1);
         const int lcd = ((st_lc >> 2) < nkb - st * KBS) ? 0 : -64;
-        dst = __builtin_amdgcn_raw_buffer_load_b128(q < QA ? ra : rb, q_off[q] + lcd, (kb0 + st * KBS) * 64, 0);
+        if (q < QA)
+            dst = __builtin_amdgcn_raw_buffer_load_b128(ra, q_off[q] + lcd, (kb0 + st * KBS) * 64, 0);
+        else
+            dst = __builtin_amdgcn_raw_buffer_load_b128(rb, q_off[q] + lcd, (kb0 + st * KBS) * 64, WNT ? kNonTemporal : 0);
     };
     auto piece_store = [&](const i32x4& src, int slot_, int q) __attribute__((always_inline)) {
         *reinterpret_cast<i32x4*>(smem + slot_ * STAGE_BYTES + 16 * t + q * 32 * ROW_BYTES) = src;
@@ -438,9 +443,12 @@ struct PanelKind {
 };
 // Wide panels for wide layers (N in the tens of thousands); narrow ones for
 // N = 5120-like layers, where a wide kind would multiply columns past the
-// panel and every wave would read all of their weight fragments.
+// panel and every wave would read all of their weight fragments.  The
+// 6 x 9 kind (328-row batches) keeps one staging set: with two it needed
+// more than 512 registers and spilled 276 bytes per lane inside the main
+// loop; with one it spills nothing and measured 1% faster.
 constexpr PanelKind kPanelKinds[] = {{1, 8, 3, 3}, {2, 8, 3, 3}, {2, 12, 3, 3}, {3, 8, 3, 3}, {4, 9, 3, 3},
-                                     {6, 9, 2, 2}, {1, 4, 3, 3}, {2, 3, 3, 3}, {2, 4, 3, 3}, {2, 5, 3, 3},
+                                     {6, 9, 1, 2}, {1, 4, 3, 3}, {2, 3, 3, 3}, {2, 4, 3, 3}, {2, 5, 3, 3},
                                      {4, 5, 3, 3}};
 constexpr int kNumPanelKinds = sizeof(kPanelKinds) / sizeof(kPanelKinds[0]);
 
@@ -515,7 +523,7 @@ bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
 
 namespace {
 
-template <int MW, int NB, int NSET, int NSLOT>
+template <int MW, int NB, int NSET, int NSLOT, bool WNT = false>
 hipError_t launch_panel_t(const GemmArgs& a, const PanelPlan& p, int32_t* partials, hipStream_t stream) {
     const int64_t cb = (a.N + 15) / 16;
     PanelParams pp;
@@ -530,7 +538,7 @@ hipError_t launch_panel_t(const GemmArgs& a, const PanelPlan& p, int32_t* partia
     pp.S = p.S;
     pp.kb_per_split = p.kb_per_split;
     const unsigned nblocks = static_cast<unsigned>(static_cast<int64_t>(p.P) * p.R * p.S);
-    hipLaunchKernelGGL((gemm_panel<MW, NB, NSET, NSLOT>), dim3(nblocks), dim3(PANEL_THREADS), 0, stream, a.xq, a.sx,
+    hipLaunchKernelGGL((gemm_panel<MW, NB, NSET, NSLOT, WNT>), dim3(nblocks), dim3(PANEL_THREADS), 0, stream, a.xq, a.sx,
                        a.w, a.sw, a.residual, a.y, partials, pp);
     return hipGetLastError();
 }
@@ -563,14 +571,22 @@ hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, 
     if (!panel_plan_valid(a.M, a.N, a.K, p)) return hipErrorInvalidValue;
     int32_t* partials = a.acc_out ? a.acc_out : p.S > 1 ? static_cast<int32_t*>(workspace) : nullptr;
     if (a.acc_out && p.S > 1) return hipErrorInvalidValue;
+    // The wide kinds stream their weights past the caches when every weight
+    // byte is read by one workgroup (no row or K splits) of a wide layer:
+    // measured 3-5% faster at N = 34816, and slower where row splits read a
+    // panel twice or N is narrow.
+    const bool wnt = p.R == 1 && p.S == 1 && a.N >= 16384;
     hipError_t e = hipErrorInvalidValue;
     switch (p.kind) {
         case 0: e = launch_panel_t<1, 8, 3, 3>(a, p, partials, stream); break;
         case 1: e = launch_panel_t<2, 8, 3, 3>(a, p, partials, stream); break;
-        case 2: e = launch_panel_t<2, 12, 3, 3>(a, p, partials, stream); break;
+        case 2: e = wnt ? launch_panel_t<2, 12, 3, 3, true>(a, p, partials, stream)
+                        : launch_panel_t<2, 12, 3, 3>(a, p, partials, stream); break;
         case 3: e = launch_panel_t<3, 8, 3, 3>(a, p, partials, stream); break;
-        case 4: e = launch_panel_t<4, 9, 3, 3>(a, p, partials, stream); break;
-        case 5: e = launch_panel_t<6, 9, 2, 2>(a, p, partials, stream); break;
+        case 4: e = wnt ? launch_panel_t<4, 9, 3, 3, true>(a, p, partials, stream)
+                        : launch_panel_t<4, 9, 3, 3>(a, p, partials, stream); break;
+        case 5: e = wnt ? launch_panel_t<6, 9, 1, 2, true>(a, p, partials, stream)
+                        : launch_panel_t<6, 9, 1, 2>(a, p, partials, stream); break;
         case 6: e = launch_panel_t<1, 4, 3, 3>(a, p, partials, stream); break;
         case 7: e = launch_panel_t<2, 3, 3, 3>(a, p, partials, stream); break;
         case 8: e = launch_panel_t<2, 4, 3, 3>(a, p, partials, stream); break;

@@ -15,7 +15,8 @@
 //   - a wave owns 16 weight rows (output columns) and all M activation rows,
 //     as R = ceil(M/16) v_mfma_i32_16x16x64_i8 accumulators;
 //   - weight fragments stream straight from HBM into VGPRs, 16 bytes per
-//     lane.  U K-steps of 64 bytes are one batch: every row of the wave gets
+//     lane (plain loads: the non-temporal policy measured 8-27% slower here,
+//     unlike the LDS-staged stream below).  U K-steps of 64 bytes are one batch: every row of the wave gets
 //     U*64 contiguous bytes.  The activation fragments of the same K-steps are
 //     loaded in the same batch, and the next batch is in flight while the
 //     current one multiplies.  No LDS, no barrier;
@@ -217,6 +218,8 @@ __global__ __launch_bounds__(KSPLIT > 1 ? 64 * KSPLIT : 256) void gemm_skinny(
 // flight: 4 waves x 4 stages of 256-byte rows (two workgroups per CU) took
 // the 3 x 248000 x 5120 read-out from 216.7 to 211.9 us; 512- and 1024-byte
 // rows per stage, with fewer waves or stages, were slower (223-349 us).
+// The copies carry the non-temporal cache policy: streaming the lm_head past
+// the caches took the read-out from 211 to 189 us (0.84 of HBM peak).
 //   Stage t holds K-bytes [RB t, RB (t+1)) of the wave's 16 rows.  Copy
 // instruction j (0..KS-1) covers rows RPI*j .. RPI*j + RPI-1 (RPI = 16/KS):
 // lane l reads row r = RPI*j + l/CPR (CPR = 4*KS chunks of 16 bytes per row
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(64 * WL_WAVES) void gemm_skinny_wlds(
         lds_i8* const dst = ring + (t % WL_NST) * WL_STAGE;
         const int8_t* const src = wbase + t * WL_RB;
 #pragma unroll
-        for (int j = 0; j < WL_KSTEPS; ++j) lds_fill16(src, woff[j], dst + j * 1024);
+        for (int j = 0; j < WL_KSTEPS; ++j) lds_fill16_nt(src, woff[j], dst + j * 1024);   // read once: streamed
     };
     // fragment of K-step s of a stage: row r = lane & 15, chunk 4s + lane/16
     const int fr = lane & 15;
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * WL_WAVES) void gemm_skinny_wlds(
     // K-steps past the last whole stage, straight from memory
     const int8_t* const wp = W + min(n0 + (lane & 15), N - 1) * K + kq;
     for (int64_t s = nstages * WL_KSTEPS; s < (K >> 6); ++s) {
-        const i32x4 wv = *reinterpret_cast<const i32x4*>(wp + s * 64);
+        const i32x4 wv = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp + s * 64));
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_frag(s), wv, acc, 0, 0, 0);
     }
 
@@ -367,12 +370,17 @@ hipError_t launch_rk(const SkinnyArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool skinny_streams_lds(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = (N + 15) / 16;
+    return M >= 1 && M <= 16 && M * (K + 16) <= kSkinnyLdsBytes && tiles >= 1024 && K >= WL_RB &&
+           K * 16 < (int64_t(1) << 32);
+}
+
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t stream) {
     if (a.M <= 0 || a.N <= 0) return hipSuccess;
     const int64_t tiles = (a.N + 15) / 16;
     const int64_t a_bytes = a.M * (a.K + 16);
-    if (a.M <= 16 && a_bytes <= kSkinnyLdsBytes && !a.gather && a.owner_c == 0 && tiles >= 1024 &&
-        a.K >= WL_RB && a.K * 16 < (int64_t(1) << 32)) {
+    if (!a.gather && a.owner_c == 0 && skinny_streams_lds(a.M, a.N, a.K)) {
         const size_t lds = static_cast<size_t>(WL_WAVES * WL_RING + a_bytes);
         hipLaunchKernelGGL(gemm_skinny_wlds, dim3(static_cast<unsigned>((tiles + WL_WAVES - 1) / WL_WAVES)),
                            dim3(64 * WL_WAVES), lds, stream, a.xq, a.sx, a.w, a.sw, a.residual, a.y, a.M, a.N,

@@ -63,6 +63,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk);
 // Override of the kernel choice: -1 automatic, 0..TILE_KINDS-1 one tiled
 // configuration, PANEL_OVERRIDE the column-panel kernel wherever it fits.
 constexpr int PANEL_OVERRIDE = TILE_KINDS;
+constexpr int SKINNY_OVERRIDE = TILE_KINDS + 1;   // the skinny kernel for every M <= SKINNY_MAX_M
 void set_tile_override(int kind);
 int tile_override_value();
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk);
@@ -94,6 +95,11 @@ hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, 
 // `gather` the weight row of output column j is gather[j]; with owner_c > 0
 // only column j of row j / owner_c is written (the candidate read-out).
 constexpr int64_t SKINNY_MAX_M = 64;
+// True when a full product of this shape streams its weights through the
+// skinny kernel's LDS rings (M <= 16 with many column tiles: the
+// full-vocabulary read-out).  There it beats the column-panel kernel; for
+// other M <= SKINNY_MAX_M the panel kernel is faster.
+bool skinny_streams_lds(int64_t M, int64_t N, int64_t K);
 
 struct SkinnyArgs {
     const int8_t* xq;

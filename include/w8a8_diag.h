@@ -21,6 +21,8 @@ extern "C" {
 
 /* w8a8_set_tile_override value that forces the column-panel kernel. */
 #define W8A8_TILE_OVERRIDE_PANEL 7
+/* w8a8_set_tile_override value that forces the skinny kernel for M <= 64. */
+#define W8A8_TILE_OVERRIDE_SKINNY 8
 
 /* Tuning and test hook (host, process-wide; the setting is one atomic
  * integer, so concurrent calls from several host threads are safe, and the
@@ -32,8 +34,10 @@ extern "C" {
  * stages, 5: as 4 with the epilogue stored straight from the accumulators,
  * 6: 256x320 with 8 waves);
  * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
- * hold the rows (by default it runs for 64 < M <= 512).  It never changes a
- * result bit, only speed.
+ * hold the rows (by default it runs for M <= 512, except the M <= 16 full
+ * products whose weights the skinny kernel streams through LDS);
+ * W8A8_TILE_OVERRIDE_SKINNY forces the skinny kernel for every M <= 64 at
+ * split-K 1.  It never changes a result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */
 int w8a8_set_tile_override(int kind);
 
@@ -41,7 +45,8 @@ int w8a8_set_tile_override(int kind);
  * Diagnostic (host, no GPU call): which kernel w8a8_gemm_splitk would run
  * for this shape, split bound and residual flag (w8a8_gemm is splitk 1),
  * under the current tile override.  out: host int32[10], filled as
- *   out[0] = 0: skinny kernel (M <= 64); rest 0.
+ *   out[0] = 0: skinny kernel (M <= 64: the full-vocabulary-style LDS stream,
+ *              or when forced); rest 0.
  *   out[0] = 1: tiled kernel; out[1] tile configuration, out[2] and out[3]
  *            the tile's rows and columns, out[4] the K splits; rest 0.
  *   out[0] = 2: column-panel kernel; out[1] its configuration, out[2] row

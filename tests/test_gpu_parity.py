@@ -220,11 +220,12 @@ def _gemm_case(M, N, K, seed, residual):
 
 
 SHAPES = [
-    (1, 7, 64), (3, 256, 320), (16, 256, 256), (64, 130, 192),      # skinny kernel
-    (3, 300, 2048), (40, 500, 2560), (5, 40, 4096), (16, 1000, 5120),  # skinny, K split over waves
+    (1, 7, 64), (3, 256, 320), (16, 256, 256), (64, 130, 192),      # M <= 64 (panel kernel by default)
+    (3, 300, 2048), (40, 500, 2560), (5, 40, 4096), (16, 1000, 5120),  # (skinny: K split over waves)
     (3, 20, 1024),   # two column tiles: half of the workgroup has no columns (LDS staging regression)
     (65, 100, 64), (200, 257, 192), (300, 520, 1024), (513, 264, 320), (256, 256, 256),
 ]
+SMALL_M = [s for s in SHAPES if s[0] <= 64]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -235,6 +236,26 @@ def test_gemm_matches_oracle(M, N, K, residual):
     want = oracle.gemm(xq, sx, w, sw, r)
     got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
+
+
+# The skinny kernel forced for M <= 64 (by default those shapes run on the
+# column-panel kernel, which is faster there, and the skinny kernel keeps the
+# full-vocabulary read-out and the candidate gather): its register-streamed
+# weights, the K-parallel mode and ragged tiles, bit for bit.
+@pytest.mark.parametrize("M,N,K", SMALL_M)
+@pytest.mark.parametrize("residual", [False, True])
+def test_skinny_kernel_forced_matches_oracle(M, N, K, residual):
+    say(f"skinny forced M={M} N={N} K={K} residual={residual}")
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + N + K, residual=residual)
+    want = oracle.gemm(xq, sx, w, sw, r)
+    assert B.w8a8_gemm_plan(M, N, K, 1, residual)[0] == 2   # panel by default
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_SKINNY)
+    try:
+        assert B.w8a8_gemm_plan(M, N, K, 1, residual)[0] == 0
+        got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+    finally:
+        B.set_tile_override(-1)
+    assert_bits_equal(got, want, f"skinny forced {M}x{N}x{K}")
 
 
 # At least 1024 column tiles and activation rows that fit in LDS: the weight

@@ -157,9 +157,6 @@ def test_panel_plan_forced_small_and_ragged():
     try:
         for M, N, K, S in itertools.product([1, 15, 16, 17, 63, 64, 200], [1, 15, 17, 300], [64, 192, 1024], [1, 3]):
             plan = B.w8a8_gemm_plan(M, N, K, S, 0)
-            if S == 1 and M <= 64:
-                assert plan[0] == 0   # the skinny kernel keeps M <= 64 without split-K
-                continue
             assert plan[0] == 2, (M, N, K, S, plan)
             check_plan(M, N, K, plan)
     finally:
@@ -167,8 +164,17 @@ def test_panel_plan_forced_small_and_ragged():
 
 
 def test_panel_default_range():
-    """By default the panel kernel takes 64 < M <= 512 and nothing else."""
-    assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 0
+    """By default the panel kernel takes M <= 512, except full products with
+    M <= 16 whose weights the skinny kernel
+    streams through LDS (the full-vocabulary read-out): at least 1024 column
+    tiles and M rows of K + 16 bytes within 40 KiB."""
+    assert B.w8a8_gemm_plan(1, 4096, 1024, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(3, 248000, 5120, 1, 0)[0] == 0
+    assert B.w8a8_gemm_plan(7, 16384, 5120, 1, 0)[0] == 0    # 7 rows of K + 16 bytes fit 40 KiB of LDS
+    assert B.w8a8_gemm_plan(8, 16384, 5120, 1, 0)[0] == 2    # 8 do not
+    assert B.w8a8_gemm_plan(7, 16368, 5120, 1, 0)[0] == 2    # 1023 column tiles
+    assert B.w8a8_gemm_plan(3, 248000, 5120, 2, 0)[0] == 2   # split-K: not the skinny kernel
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 1
@@ -178,3 +184,9 @@ def test_panel_default_range():
             assert B.w8a8_gemm_plan(256, 34816, 5120, 1, 0)[0] == 1
         finally:
             B.set_tile_override(-1)
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_SKINNY)
+    try:
+        assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 0
+        assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 1
+    finally:
+        B.set_tile_override(-1)
