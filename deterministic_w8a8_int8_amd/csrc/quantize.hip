@@ -194,7 +194,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
     if (n256 <= 2) return launch_reg<2, 256, 1, false, 8>(a, stream);
     if (n256 <= 3) return launch_reg<3, 256, 1, false, 8>(a, stream);
     if (n256 <= 4) return launch_reg<4, 256, 1, false, 8>(a, stream);
-    if (n256 <= 5) return launch_reg<5, 256, 1, false, 7>(a, stream);
+    if (n256 <= 5) return launch_reg<5, 256, 1, false, 8>(a, stream);
     if (n256 <= 6) return launch_reg<6, 256, 1, false, 6>(a, stream);
     if (n512 <= 4) return launch_reg<4, 512, 1, false, 8>(a, stream);
     if (n512 <= 5) return launch_reg<5, 512, 1, false, 6>(a, stream);
