@@ -418,7 +418,10 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
                     v.z = scale_acc(a[2], sxm, s2);
                     v.w = scale_acc(a[3], sxm, s3);
                 }
-                *reinterpret_cast<float4*>(y + o) = v;
+                // non-temporal: every workgroup writes its outputs in the same
+                // burst at the end, and streamed stores drain that burst 5-9%
+                // faster (short-request gate+up 68 -> 62 us)
+                store_out4(y + o, v, true);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
