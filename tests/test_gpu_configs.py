@@ -223,6 +223,7 @@ def test_batch_invariance_stress():
             if ref is None:
                 ref = [o.clone() for o in outs]
                 canon_xq, canon_sx, canon_starts = host(xq), host(sx), starts
+                canon_x, canon_y = xa, y.clone()
             else:
                 for i, o in enumerate(outs):
                     assert torch.equal(o.view(torch.int32), ref[i].view(torch.int32)), \
@@ -243,7 +244,14 @@ def test_batch_invariance_stress():
     got = np.array([host(ref[q][int(m - canon_starts[q]), int(n)]) for q, m, n in zip(req_of, mi, ni)],
                    dtype=np.float32)
     assert_bits_equal(got, want, "stress sampled")
-    # and the quantised rows themselves against the oracle on one request
-    xq_o, sx_o = oracle.quantize_act(reqs[0], layer["smooth"])
-    s0 = int(canon_starts[0])
-    assert np.array_equal(canon_xq[s0:s0 + reqs[0].shape[0]], xq_o)
+    # the whole canonical batch (pad rows included): one output in every
+    # 32 x 32 block of the tiled kernel's output, and every quantised row
+    M = canon_y.shape[0]
+    bi, bj = synth.block_points(np.random.default_rng(52), M, N, 32, 32)
+    say(f"stress: {bi.size} block samples over {M}x{N}")
+    got = host(canon_y[torch.from_numpy(bi).cuda(), torch.from_numpy(bj).cuda()])
+    want = oracle.gemm_sampled(canon_xq, canon_sx, layer["w"], layer["sw"], bi, bj)
+    assert_bits_equal(got, want, "stress block samples")
+    xq_o, sx_o = oracle.quantize_act(canon_x, layer["smooth"])
+    assert_bits_equal(canon_sx, sx_o, "stress sx")
+    assert np.array_equal(canon_xq, xq_o), "stress quantised rows differ"
