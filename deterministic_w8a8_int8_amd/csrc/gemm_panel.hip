@@ -506,7 +506,11 @@ bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
                                    4.0 * M * N * (residual ? 2.0 : 1.0);
                 if (S > 1) hbm_bytes += 4.0 * S * M * N;
                 t = std::max(t, hbm_bytes / hbm + 8e-6);
-                if (S > 1) t += 3e-6 + (4.0 * S + 8.0) * M * N / 4.0e12;   // reduction kernel
+                // reduction kernel: a second launch (about 5 us) and its stream.
+                // Calibrated against every feasible plan of 40 mid-M shapes
+                // timed on MI355X: with 3 us the planner split a 128 x 5120 x
+                // 5120 product four ways (20 us) where one way takes 12.5 us
+                if (S > 1) t += 5e-6 + (4.0 * S + 8.0) * M * N / 4.0e12;
                 if (t < best * 0.999) {
                     best = t;
                     bp.kind = kind;
