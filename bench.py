@@ -468,7 +468,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by rows or output columns with no communication; see DESIGN.md)",
+              "(the path shards by rows or output columns with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
