@@ -92,8 +92,9 @@ __global__ __launch_bounds__(T) void answer_head_kernel(
     const float no_max[1] = {0.0f};
     float scale1[1];
     bool valid1[1];
-    quantize_rows_regs<NV, T, 1, false, true>(
-        xv, rv, sv, odd_t, s4, K4, ok1, no_max, red,
+    quantize_rows_regs<NV, T, 1, false>(
+        xv, [&](int i) __attribute__((always_inline)) { return rv[i]; },
+        [&](int i, int) __attribute__((always_inline)) { return sv[i]; }, odd_t, K4, ok1, no_max, red,
         [&](int, int i, uint32_t packed) __attribute__((always_inline)) {
             q[i] = packed;   // kept for the candidate dot products
             qr[t + i * T] = packed;

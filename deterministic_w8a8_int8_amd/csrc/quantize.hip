@@ -98,8 +98,13 @@ __global__ __launch_bounds__(T, WAVES) void quantize_rows_reg(
 
     float scale[R];
     bool valid[R];
-    quantize_rows_regs<NV, T, R, GIVEN, KEEP>(
-        xv, rv, sv, odd_t, s4, K4, ok, amax_g, red,
+    quantize_rows_regs<NV, T, R, GIVEN>(
+        xv, [&](int i) __attribute__((always_inline)) { return rv[i]; },
+        [&](int i, int j) __attribute__((always_inline)) {
+            if constexpr (KEEP) return sv[i];
+            else return s4[j];
+        },
+        odd_t, K4, ok, amax_g, red,
         [&](int r, int i, uint32_t packed) __attribute__((always_inline)) {
             if (live[r]) reinterpret_cast<uint32_t*>(xq + (m0 + r) * K)[t + i * T] = packed;
         },

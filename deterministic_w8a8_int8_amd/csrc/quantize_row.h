@@ -144,14 +144,17 @@ __device__ __forceinline__ uint32_t pack4i(int a, int b, int c, int d) {
            ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
 }
 
-// Quantise R rows held in registers at once (xv[r], as load_row leaves them;
-// rv, sv and odd_t as load_smoothing leaves them).  The codes of float4
-// number t + T*i of row r (four int8 packed little-endian) are handed to
-// emit(r, i, packed) as soon as they are final (for t + T*i < K/4), so the
-// caller decides whether they are stored at once or kept.  scale[r] is the
-// token scale fl(amax/127) (0 for an invalid row); valid[r] is false for
-// ok[r] == false or a row without a finite maximum.  GIVEN: the maximum is
-// amax_given[r] instead of the row's own.  One barrier for all R rows (the
+// Quantise R rows held in registers at once (xv[r], as load_row leaves
+// them).  rv_at(i) returns the reciprocals of the smoothing values of the
+// thread's float4 number t + T*i, sv_at(i, j) the smoothing values themselves
+// (j = t + T*i, the float4 index in the row), and odd_t is as load_smoothing
+// leaves it: the caller decides where they live (registers, LDS or memory).
+// The codes of float4 t + T*i of row r (four int8 packed little-endian) are
+// handed to emit(r, i, packed) as soon as they are final (for t + T*i < K/4),
+// so the caller decides whether they are stored at once or kept.  scale[r]
+// is the token scale fl(amax/127) (0 for an invalid row); valid[r] is false
+// for ok[r] == false or a row without a finite maximum.  GIVEN: the maximum
+// is amax_given[r] instead of the row's own.  One barrier for all R rows (the
 // block-wide maxima through red[R * NW]).
 //
 // The work per element is kept small, since at HBM speed the scan has few
@@ -162,15 +165,11 @@ __device__ __forceinline__ uint32_t pack4i(int a, int b, int c, int d) {
 // overflow of the sum only sends the wave down the exact path); and the code
 // pass takes one branch per float4, to the exact divisions, when any of its
 // four values lies near a rounding boundary.
-template <int NV, int T, int R, bool GIVEN, bool KEEP, class Emit>
-__device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], const float4 (&rv)[NV],
-                                                   const float4 (&sv)[NV], bool odd_t, const float4* s4, int K4,
-                                                   const bool (&ok)[R], const float (&amax_given)[R], float* red,
-                                                   Emit&& emit, float (&scale)[R], bool (&valid)[R]) {
-    auto smooth4 = [&](int i, int j) __attribute__((always_inline)) {
-        if constexpr (KEEP) return sv[i];
-        else return s4[j];
-    };
+template <int NV, int T, int R, bool GIVEN, class RvAt, class SvAt, class Emit>
+__device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], RvAt&& rv_at, SvAt&& smooth4,
+                                                   bool odd_t, int K4, const bool (&ok)[R],
+                                                   const float (&amax_given)[R], float* red, Emit&& emit,
+                                                   float (&scale)[R], bool (&valid)[R]) {
     constexpr int NW = T / 64;
     const int t = threadIdx.x;
     float amax[R];
@@ -188,7 +187,7 @@ __device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], co
             fin[r] = 0.0f;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const float4 ap = mul4(xv[r][i], rv[i]);
+                const float4 ap = mul4(xv[r][i], rv_at(i));
                 m4[r][i] = max4abs(ap);
                 amax_loc[r] = fmaxf(amax_loc[r], m4[r][i]);
                 fin[r] += (ap.x + ap.y) + (ap.z + ap.w);
@@ -216,7 +215,7 @@ __device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], co
             for (int i = 0; i < NV; ++i) {
                 const int j = t + i * T;
                 if (j < K4 && (all_exact || m4[r][i] >= thresh)) {
-                    const float4 ap = mul4(xv[r][i], rv[i]);
+                    const float4 ap = mul4(xv[r][i], rv_at(i));
                     const float4 sv4 = smooth4(i, j);
                     const float xs[4] = {xv[r][i].x, xv[r][i].y, xv[r][i].z, xv[r][i].w};
                     const float as[4] = {ap.x, ap.y, ap.z, ap.w};
@@ -258,7 +257,7 @@ __device__ __forceinline__ void quantize_rows_regs(const float4 (&xv)[R][NV], co
                 const float4 x = xv[r][i];
                 bool near = exact;
                 if (!exact) {
-                    const float4 rr = rv[i];
+                    const float4 rr = rv_at(i);
                     packed = pack4i(fast_code(x.x, rr.x, inv, near), fast_code(x.y, rr.y, inv, near),
                                     fast_code(x.z, rr.z, inv, near), fast_code(x.w, rr.w, inv, near));
                 }
