@@ -167,12 +167,14 @@ hipError_t launch_answer_head(const AnswerHeadArgs& a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     const int64_t n256 = (a.K + 1023) / 1024;   // float4 per thread with 256 threads
     const int64_t n512 = (a.K + 2047) / 2048;   // ... with 512 threads
+    // Past K = 2048 a row is split over 512 threads: the head is a chain of
+    // dependent phases (load, reduce, quantise, dot, reduce, softmax) on one
+    // workgroup per row, and halving each thread's share shortens every
+    // phase (K = 5120: 6.5 against 7.9 us back to back; 1024 threads: 6.7).
     if (n256 <= 1) return launch_t<1, 256>(a, stream);
     if (n256 <= 2) return launch_t<2, 256>(a, stream);
-    if (n256 <= 3) return launch_t<3, 256>(a, stream);
-    if (n256 <= 4) return launch_t<4, 256>(a, stream);
-    if (n256 <= 5) return launch_t<5, 256>(a, stream);
-    if (n256 <= 6) return launch_t<6, 256>(a, stream);
+    if (n512 <= 2) return launch_t<2, 512>(a, stream);
+    if (n512 <= 3) return launch_t<3, 512>(a, stream);
     if (n512 <= 4) return launch_t<4, 512>(a, stream);
     if (n512 <= 5) return launch_t<5, 512>(a, stream);
     if (n512 <= 6) return launch_t<6, 512>(a, stream);

@@ -158,12 +158,12 @@ def _same_or_both_nan(a, b):
 
 
 # The answer head runs as one kernel for K <= 18432 (256 threads up to K =
-# 6144, 512 above) and as three launches beyond.  Every output (quantised
+# 2048, 512 above) and as three launches beyond.  Every output (quantised
 # rows, token scales, logits, probabilities) must equal the separate calls
 # bit for bit, with bad row indices and bad candidate ids, several candidate
 # groups (C up to 64) and many answer rows; valid rows' logits must equal the
 # oracle's.
-@pytest.mark.parametrize("K,C,M", [(256, 1, 1), (1024, 4, 3), (5120, 4, 1), (5120, 7, 70), (6144, 64, 5),
+@pytest.mark.parametrize("K,C,M", [(256, 1, 1), (1024, 4, 3), (2112, 2, 2), (3072, 3, 4), (5120, 4, 1), (5120, 7, 70), (6144, 64, 5),
                                    (8192, 5, 9), (17408, 4, 3), (40960, 4, 2)])
 def test_answer_head_fused_matches_separate_calls(K, C, M):
     say(f"answer head K={K} C={C} M={M}")
