@@ -87,6 +87,7 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 // kernel (PANEL_OVERRIDE, any M it fits) or the skinny kernel
 // (SKINNY_OVERRIDE, every M <= SKINNY_MAX_M).
 constexpr int64_t kPanelMaxM = 512;
+constexpr int64_t kPanelOnlyM = 384;   // up to here no comparison: the panel kernel won on every measured shape
 static_assert(W8A8_TILE_OVERRIDE_PANEL == w8a8::PANEL_OVERRIDE, "header and library disagree on the panel override");
 static_assert(W8A8_TILE_OVERRIDE_SKINNY == w8a8::SKINNY_OVERRIDE, "header and library disagree on the skinny override");
 
@@ -94,7 +95,18 @@ bool pick_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
     const int ov = w8a8::tile_override_value();
     if (ov >= 0 && ov != w8a8::PANEL_OVERRIDE) return false;
     if (ov < 0 && M > kPanelMaxM) return false;
-    return w8a8::plan_panel(M, N, K, max_splitk, residual, pp);
+    if (!w8a8::plan_panel(M, N, K, max_splitk, residual, pp)) return false;
+    // Past 384 rows the panels of a wide layer no longer fit one round of
+    // workgroups (448 x 34816 x 5120: two rounds, 106 us) while the tiled
+    // kernel still needs one (88 us).  There the tiled kernel runs when its
+    // time model is clearly below the panel's on a product that is not
+    // launch-bound.  Calibrated on 14 shapes of 384-512 rows: the tiled
+    // kernel wins for N = 25000 and 34816 (by 17-21%), the panel kernel for
+    // N = 5120, 15360 and 20000 and for products of a few microseconds.
+    if (ov < 0 && M > kPanelOnlyM && pp->est_us > 40.0 &&
+        w8a8::tiled_time_estimate_us(M, N, K, max_splitk) < 0.75 * pp->est_us)
+        return false;
+    return true;
 }
 
 // The skinny kernel for a full product at split-K 1 (see above); otherwise

@@ -1127,6 +1127,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk) {
     return p;
 }
 
+double tiled_time_estimate_us(int64_t M, int64_t N, int64_t K, int splitk) {
+    const GemmPlan p = plan_gemm(M, N, K, splitk);
+    const KindInfo& k = kKinds[p.kind];
+    const int64_t blocks = p.tiles_m * p.tiles_n * splitk;
+    const int64_t slots = static_cast<int64_t>(256) * k.per_cu;
+    const int64_t rounds = (blocks + slots - 1) / slots;
+    const int64_t kps = (K / 64 + splitk - 1) / splitk * 64;
+    // int8 operations per second per CU: 256x320 tiles sustain 10.1e12
+    // (one round of 218 tiles at K = 5120 takes 91 us, 8 of them launch,
+    // prologue and epilogue); the other configurations in proportion to
+    // their weights above
+    const double rate = 10.1e12 * k.weight / kKinds[TILE_KIND_6].weight;
+    double t = static_cast<double>(rounds) * 2.0 * k.bm * k.bn * static_cast<double>(kps) * k.per_cu / rate + 8e-6;
+    if (splitk > 1) t += 5e-6 + (4.0 * splitk + 8.0) * static_cast<double>(M) * static_cast<double>(N) / 4.0e12;
+    return t * 1e6;
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int splitk) {
     if (splitk <= 1) return 0;
     // S row-major int32 slices of the output, rounded up to 256 bytes

@@ -60,6 +60,10 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, int splitk);
+// Time model of the tiled kernel (us) for routing against the column-panel
+// kernel: rounds of full tiles at the per-CU rate measured for 256x320
+// tiles, plus launch, prologue and epilogue, plus the split-K reduction.
+double tiled_time_estimate_us(int64_t M, int64_t N, int64_t K, int splitk);
 // Override of the kernel choice: -1 automatic, 0..TILE_KINDS-1 one tiled
 // configuration, PANEL_OVERRIDE the column-panel kernel wherever it fits.
 constexpr int PANEL_OVERRIDE = TILE_KINDS;

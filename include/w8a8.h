@@ -140,8 +140,9 @@ size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int spl
  * w8a8_gemm_splitk -- the same result as w8a8_gemm, with K cut into at
  * most `splitk` contiguous chunks (review page, section "Bitwise
  * consistency is not lossless quantization": split-K partial sums stay
- * integers).  With S chunks (S = splitk for M > 512; for 64 < M <= 512 the
- * column-panel kernel picks S <= splitk for speed, see w8a8_gemm_plan):
+ * integers).  With S chunks (S = splitk on the tiled kernel; the column-panel
+ * kernel, which runs most products of up to 512 rows, picks S <= splitk for
+ * speed; w8a8_gemm_plan reports which):
  *     chunk c covers k in [c*Kc, min((c+1)*Kc, K)), Kc = ceil(K/S)
  *     rounded up to a multiple of 64 (of 128 on the panel kernel);
  *     P_c[m,n] = sum over chunk c of xq[m,k]*w[n,k]      (int32)

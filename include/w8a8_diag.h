@@ -35,7 +35,9 @@ extern "C" {
  * 6: 256x320 with 8 waves);
  * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
  * hold the rows (by default it runs for M <= 512, except the M <= 16 full
- * products whose weights the skinny kernel streams through LDS);
+ * products whose weights the skinny kernel streams through LDS, and past 384
+ * rows the wide layers whose panels would need two rounds of workgroups,
+ * which the tiled kernel runs in one);
  * W8A8_TILE_OVERRIDE_SKINNY forces the skinny kernel for every M <= 64 at
  * split-K 1.  It never changes a result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */

@@ -240,6 +240,25 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
+# Between 384 and 512 rows a wide layer runs on the tiled kernel (its panels
+# would need two rounds of workgroups), a narrower one on the panel kernel:
+# both sides of the crossover, sampled in every 16 x 16 output block (and in
+# two whole rows) against the oracle, with the route checked.
+@pytest.mark.parametrize("M,N,K,path", [(448, 34816, 5120, 1), (384, 34816, 5120, 2), (512, 15360, 1024, 2)])
+def test_routing_crossover_matches_oracle(M, N, K, path):
+    say(f"crossover gemm M={M} N={N} K={K}")
+    assert B.w8a8_gemm_plan(M, N, K, 1, False)[0] == path
+    xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + N, residual=True)
+    got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+    rng = np.random.default_rng(M)
+    bi, bj = synth.block_points(rng, M, N, 16, 16)
+    rows = np.array([0, M - 1])
+    mi = np.concatenate([bi, np.repeat(rows, N)])
+    ni = np.concatenate([bj, np.tile(np.arange(N), rows.size)])
+    want = oracle.gemm_sampled(xq, sx, w, sw, mi, ni, residual=r)
+    assert_bits_equal(got[mi, ni], want, f"gemm {M}x{N}x{K} (path {path})")
+
+
 # The skinny kernel forced for M <= 64 (by default those shapes run on the
 # column-panel kernel, which is faster there, and the skinny kernel keeps the
 # full-vocabulary read-out and the candidate gather): its register-streamed

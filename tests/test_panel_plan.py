@@ -144,9 +144,14 @@ SHAPES = [
 
 @pytest.mark.parametrize("M,N,K,S,res", SHAPES)
 def test_panel_plan_in_bounds(M, N, K, S, res):
-    plan = B.w8a8_gemm_plan(M, N, K, S, res)
-    if plan[0] != 2:
-        pytest.skip("shape not on the panel kernel")
+    """The panel plan of each shape (forced, so that shapes the router sends
+    to the tiled kernel, like 512 x 34816 x 5120, are checked too)."""
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_PANEL)
+    try:
+        plan = B.w8a8_gemm_plan(M, N, K, S, res)
+    finally:
+        B.set_tile_override(-1)
+    assert plan[0] == 2, (M, N, K, S, plan)
     assert 1 <= plan[4] <= S
     check_plan(M, N, K, plan)
 
@@ -167,7 +172,9 @@ def test_panel_default_range():
     """By default the panel kernel takes M <= 512, except full products with
     M <= 16 whose weights the skinny kernel
     streams through LDS (the full-vocabulary read-out): at least 1024 column
-    tiles and M rows of K + 16 bytes within 40 KiB."""
+    tiles and M rows of K + 16 bytes within 40 KiB; and, past 384 rows, wide
+    layers whose panels would need two rounds of workgroups, which the tiled
+    kernel runs in one."""
     assert B.w8a8_gemm_plan(1, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(3, 248000, 5120, 1, 0)[0] == 0
@@ -178,6 +185,20 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(384, 34816, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(385, 34816, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(512, 34816, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(480, 25000, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(512, 20000, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(512, 15360, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(448, 5120, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(512, 5120, 17408, 8, 1)[0] == 2
+    assert B.w8a8_gemm_plan(500, 4096, 256, 1, 0)[0] == 2    # a few microseconds: launch-bound
+    B.set_tile_override(B.W8A8_TILE_OVERRIDE_PANEL)
+    try:
+        assert B.w8a8_gemm_plan(448, 34816, 5120, 1, 0)[0] == 2
+    finally:
+        B.set_tile_override(-1)
     for kind in range(B.W8A8_TILE_OVERRIDE_PANEL):
         B.set_tile_override(kind)
         try:
