@@ -77,7 +77,8 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 }
 
 // Kernel choice for a full product.  The column-panel kernel takes M up to
-// kPanelMaxM, except full products with M <= SKINNY_MAX_M whose weights the
+// kPanelOnlyM, and up to kPanelMaxM unless the tiled kernel's time model is
+// clearly faster (see pick_panel), except full products with M <= SKINNY_MAX_M whose weights the
 // skinny kernel streams through LDS (the full-vocabulary read-out), where
 // the skinny kernel is faster; larger M takes the tiled kernel.  Measured:
 // for M = 16..64 the panel kernel runs 1.5-3.2x faster than the skinny one
@@ -86,7 +87,7 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 // The override can force a tiled configuration (0..TILE_KINDS-1), the panel
 // kernel (PANEL_OVERRIDE, any M it fits) or the skinny kernel
 // (SKINNY_OVERRIDE, every M <= SKINNY_MAX_M).
-constexpr int64_t kPanelMaxM = 512;
+constexpr int64_t kPanelMaxM = 1024;
 constexpr int64_t kPanelOnlyM = 384;   // up to here no comparison: the panel kernel won on every measured shape
 static_assert(W8A8_TILE_OVERRIDE_PANEL == w8a8::PANEL_OVERRIDE, "header and library disagree on the panel override");
 static_assert(W8A8_TILE_OVERRIDE_SKINNY == w8a8::SKINNY_OVERRIDE, "header and library disagree on the skinny override");
@@ -96,13 +97,15 @@ bool pick_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
     if (ov >= 0 && ov != w8a8::PANEL_OVERRIDE) return false;
     if (ov < 0 && M > kPanelMaxM) return false;
     if (!w8a8::plan_panel(M, N, K, max_splitk, residual, pp)) return false;
-    // Past 384 rows the panels of a wide layer no longer fit one round of
-    // workgroups (448 x 34816 x 5120: two rounds, 106 us) while the tiled
-    // kernel still needs one (88 us).  There the tiled kernel runs when its
-    // time model is clearly below the panel's on a product that is not
-    // launch-bound.  Calibrated on 14 shapes of 384-512 rows: the tiled
-    // kernel wins for N = 25000 and 34816 (by 17-21%), the panel kernel for
-    // N = 5120, 15360 and 20000 and for products of a few microseconds.
+    // Past 384 rows the two kernels trade places by shape: the panels of a
+    // wide layer no longer fit one round of workgroups (448 x 34816 x 5120:
+    // two rounds, 106 us) while the tiled kernel still needs one (88 us);
+    // narrow layers with long K stay far faster on panels (1024 x 5120 x
+    // 17408: 110 against 193 us).  There the tiled kernel runs when its time
+    // model is clearly below the panel's on a product that is not
+    // launch-bound.  Calibrated on 30 shapes of 384-1024 rows (N from 4096
+    // to 34816, K from 256 to 17408, split-K 1 and 8): the rule picks the
+    // faster kernel on every one.
     if (ov < 0 && M > kPanelOnlyM && pp->est_us > 40.0 &&
         w8a8::tiled_time_estimate_us(M, N, K, max_splitk) < 0.75 * pp->est_us)
         return false;

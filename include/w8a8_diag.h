@@ -34,10 +34,10 @@ extern "C" {
  * stages, 5: as 4 with the epilogue stored straight from the accumulators,
  * 6: 256x320 with 8 waves);
  * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
- * hold the rows (by default it runs for M <= 512, except the M <= 16 full
- * products whose weights the skinny kernel streams through LDS, and past 384
- * rows the wide layers whose panels would need two rounds of workgroups,
- * which the tiled kernel runs in one);
+ * hold the rows (by default it runs for M <= 384, except the M <= 16 full
+ * products whose weights the skinny kernel streams through LDS, and for
+ * 385 <= M <= 1024 unless a time model puts the tiled kernel clearly ahead,
+ * as for wide layers whose panels would need two rounds of workgroups);
  * W8A8_TILE_OVERRIDE_SKINNY forces the skinny kernel for every M <= 64 at
  * split-K 1.  It never changes a result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */

@@ -56,10 +56,14 @@ def test_gemm_at_the_int32_bound(M, N):
     assert_bits_equal(host(B.w8a8_gemm(*d)), want, f"gemm max K (path {plan[0]})")
     assert_bits_equal(host(B.w8a8_gemm_splitk(*d, 5)), want, "gemm max K split-K 5")
     assert np.array_equal(host(B.w8a8_gemm_int32(d[0], d[2])), acc), "int32 accumulators at max K"
+    # every kernel, whichever the router picks for this shape
+    forced = [(6, "tiled 256x320"), (B.W8A8_TILE_OVERRIDE_PANEL, "panel")]
     if M <= 64:
-        B.set_tile_override(B.W8A8_TILE_OVERRIDE_SKINNY)
+        forced.append((B.W8A8_TILE_OVERRIDE_SKINNY, "skinny"))
+    for kind, name in forced:
+        B.set_tile_override(kind)
         try:
-            assert_bits_equal(host(B.w8a8_gemm(*d)), want, "skinny forced, max K")
+            assert_bits_equal(host(B.w8a8_gemm(*d)), want, f"{name} forced, max K")
         finally:
             B.set_tile_override(-1)
 

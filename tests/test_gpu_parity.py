@@ -224,6 +224,7 @@ SHAPES = [
     (3, 300, 2048), (40, 500, 2560), (5, 40, 4096), (16, 1000, 5120),  # (skinny: K split over waves)
     (3, 20, 1024),   # two column tiles: half of the workgroup has no columns (LDS staging regression)
     (65, 100, 64), (200, 257, 192), (300, 520, 1024), (513, 264, 320), (256, 256, 256),
+    (1100, 300, 256), (1537, 70, 448),      # past 1024 rows: the tiled kernel by default
     (48, 20000, 512), (130, 17000, 320),    # narrow-kind panels over many columns
     (40, 34816, 256), (160, 34816, 256),    # wide kinds with the non-temporal weight stream
 ]
@@ -240,14 +241,16 @@ def test_gemm_matches_oracle(M, N, K, residual):
     assert_bits_equal(got, want, f"gemm {M}x{N}x{K}")
 
 
-# Between 384 and 512 rows a wide layer runs on the tiled kernel (its panels
-# would need two rounds of workgroups), a narrower one on the panel kernel:
-# both sides of the crossover, sampled in every 16 x 16 output block (and in
-# two whole rows) against the oracle, with the route checked.
-@pytest.mark.parametrize("M,N,K,path", [(448, 34816, 5120, 1), (384, 34816, 5120, 2), (512, 15360, 1024, 2)])
+# Between 385 and 1024 rows the two GEMM kernels' time models pick the
+# kernel: a wide layer of 448 rows runs on the tiled kernel (its panels would
+# need two rounds of workgroups), a long-K narrow layer of 1024 rows on the
+# panel kernel.  Both sides of the crossover, sampled in every 16 x 16 output
+# block (and in two whole rows) against the oracle, with the route checked.
+@pytest.mark.parametrize("M,N,K,path", [(448, 34816, 5120, 1), (384, 34816, 5120, 2), (512, 15360, 1024, 2),
+                                        (1024, 5120, 17408, 2), (896, 15360, 5120, 1)])
 def test_routing_crossover_matches_oracle(M, N, K, path):
     say(f"crossover gemm M={M} N={N} K={K}")
-    assert B.w8a8_gemm_plan(M, N, K, 1, False)[0] == path
+    assert B.w8a8_gemm_plan(M, N, K, 1, True)[0] == path
     xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + N, residual=True)
     got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
     rng = np.random.default_rng(M)

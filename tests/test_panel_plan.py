@@ -169,12 +169,12 @@ def test_panel_plan_forced_small_and_ragged():
 
 
 def test_panel_default_range():
-    """By default the panel kernel takes M <= 512, except full products with
+    """By default the panel kernel takes M <= 384, except full products with
     M <= 16 whose weights the skinny kernel
     streams through LDS (the full-vocabulary read-out): at least 1024 column
-    tiles and M rows of K + 16 bytes within 40 KiB; and, past 384 rows, wide
-    layers whose panels would need two rounds of workgroups, which the tiled
-    kernel runs in one."""
+    tiles and M rows of K + 16 bytes within 40 KiB.  From 385 to 1024 rows
+    the two kernels' time models decide (the decisions below are the faster
+    kernel as measured on MI355X); past 1024 rows the tiled kernel runs."""
     assert B.w8a8_gemm_plan(1, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(3, 248000, 5120, 1, 0)[0] == 0
@@ -184,7 +184,16 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(3, 248000, 5120, 2, 0)[0] == 2   # split-K: not the skinny kernel
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
-    assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(1025, 4096, 1024, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(640, 34816, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(768, 15360, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(896, 34816, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(896, 15360, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(1024, 5120, 17408, 1, 1)[0] == 2
+    assert B.w8a8_gemm_plan(1024, 5120, 17408, 8, 1)[0] == 2
+    assert B.w8a8_gemm_plan(1024, 5120, 5120, 1, 0)[0] == 2
+    assert B.w8a8_gemm_plan(1025, 5120, 17408, 1, 1)[0] == 1
     assert B.w8a8_gemm_plan(384, 34816, 5120, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(385, 34816, 5120, 1, 0)[0] == 1
     assert B.w8a8_gemm_plan(512, 34816, 5120, 1, 0)[0] == 1
