@@ -1039,7 +1039,11 @@ hipError_t launch_reduce(const GemmArgs& a, int S, const int32_t* partials, hipS
 namespace {
 
 // The configurations, indexed by TileKind.
-using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1>;  // 256x256, 4 waves, 128-byte stages x2
+// 256x256, 4 waves of 128x128 on 16x16x64 MFMAs (256 accumulator registers
+// a wave), 128-byte stages x2.  With 32x32x32 MFMAs this configuration spilled
+// 308 bytes per lane and ran 4x slower; never chosen automatically (the 8-wave
+// 256x256 configuration is faster), kept as a forced alternative.
+using Cfg0 = Cfg<2, 2, 4, 4, 128, 2, 1, false, true, 2, true>;
 using Cfg1 = Cfg<2, 4, 4, 2, 64, 4, 1>;   // 256x256, 8 waves, 64-byte stages x4
 using Cfg2 = Cfg<2, 2, 4, 2, 64, 3, 2>;   // 256x128, 4 waves, 2 workgroups per CU
 using Cfg3 = Cfg<2, 2, 2, 2, 64, 4, 2>;   // 128x128, 4 waves, 2 workgroups per CU

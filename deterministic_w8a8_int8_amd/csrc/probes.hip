@@ -61,10 +61,17 @@ template <int KIND, bool MF16>
 __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sink, int64_t iters) {
     const uint32_t t = threadIdx.x + blockIdx.x * CEIL_THREADS;
     i32x4 a[4][4], b[4][2];
+    // the operand loops unrolled, so that the operands live in registers
+    // (indexed dynamically they were placed in scratch memory); the byte
+    // loop stays rolled (unrolled, its hash arithmetic spilled)
+#pragma unroll
     for (int s = 0; s < 4; ++s) {
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
+#pragma unroll
             for (int e = 0; e < 4; ++e) {
                 uint32_t w = 0;
+#pragma nounroll
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t h = mix32(t * 4096u + s * 256u + i * 16u + e * 4u + q);
                     const int v = KIND == 0 ? static_cast<int>(h & 255u) - 128 : activation_like_byte(h);
@@ -73,7 +80,9 @@ __global__ __launch_bounds__(CEIL_THREADS) void mfma_ceiling_kernel(int32_t* sin
                 a[s][i][e] = static_cast<int32_t>(w);
             }
         }
+#pragma unroll
         for (int j = 0; j < 2; ++j)
+#pragma unroll
             for (int e = 0; e < 4; ++e) b[s][j][e] = static_cast<int32_t>(mix32(t * 4096u + 2048u + s * 64u + j * 8u + e));
     }
     int32_t x = 0;

@@ -28,7 +28,8 @@ extern "C" {
  * integer, so concurrent calls from several host threads are safe, and the
  * last one wins): force the tile configuration of the tiled GEMM for later
  * calls.  -1 = automatic (the default); 0..6 pick
- * one of the configurations of the tiled kernel (0: 256x256 with 4 waves, 1:
+ * one of the configurations of the tiled kernel (0: 256x256 with 4 waves on
+ * 16x16x64 MFMAs, 1:
  * 256x256 with 8 waves and a 4-stage pipeline, 2: 256x128 with two
  * workgroups per CU, 3: 128x128, 4: 256x256 with 8 waves and 128-byte
  * stages, 5: as 4 with the epilogue stored straight from the accumulators,
