@@ -56,10 +56,10 @@ def check_layer(d, *, splits=(1,), rows_full=2, seed=0, label=""):
         del ys
     rng = np.random.default_rng(seed)
     mi, ni = synth.sample_points(rng, M, N, N_SAMPLES)
-    # plus one output in every 16 x 16 block (M <= 512: the skinny and panel
-    # kernels' row groups and 16-column wave strips) or 32 x 32 block (the
-    # tiled kernel's per-wave MFMA tiles), so every tile is touched
-    blk = 16 if M <= 512 else 32
+    # plus one output in every 16 x 16 block (the skinny and panel kernels'
+    # row groups and 16-column wave strips) or 32 x 32 block (the tiled
+    # kernel's per-wave MFMA tiles), so every tile is touched
+    blk = 32 if B.w8a8_gemm_plan(M, N, K, 1, d["r"] is not None)[0] == 1 else 16
     bi, bj = synth.block_points(rng, M, N, blk, blk)
     mi, ni = np.concatenate([mi, bi]), np.concatenate([ni, bj])
     say(f"{label}: {mi.size} sampled outputs")
