@@ -16,7 +16,11 @@ MFMA peak.  Its duration is measured with HIP events around every launch of
 that kernel inside the timed steps.  ``readout`` reports the full-vocabulary
 skinny GEMM (M = 3 answer rows x 248000 lm_head rows), which is HBM-bound,
 against HBM bandwidth.  That is the general path the candidate read-out
-replaces, timed in the same run.  ``mfma_ceiling`` is the throughput the
+replaces, timed in the same run; ``readout.candidates_us`` is the
+candidate-only read-out of the same rows (C candidates each), with events
+around each launch (for so short a kernel that is mostly the host's time
+per call) and back to back, and ``candidates_speedup_vs_full`` the full
+read-out's time over the back-to-back one.  ``mfma_ceiling`` is the throughput the
 int8 matrix cores sustain on register-resident operands with no memory
 traffic (uniform int8, and activation-like A; 32x32x32 and 16x16x64 MFMAs),
 measured in the same run; ``roofline.frac_of_sustained_ceiling`` relates
@@ -610,11 +614,37 @@ def main():
         full_us = t.mean_us("full")
         full_bytes = head["N"] * head["K"] + 4 * head["N"] + Mr * head["K"] + 4 * Mr + 4 * Mr * head["N"]
         full_gbs = full_bytes / (full_us * 1e-6) / 1e9
+        # the same rows' candidate-only read-out (C candidates each)
+        cand3 = dev(rd["cand"])
+        lg3 = torch.empty(tuple(rd["cand"].shape), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            B.w8a8_readout_candidates(xqr, sxr, wh, swh, cand3, logits=lg3)
+        for _ in range(20):
+            t.run("cand", lambda: B.w8a8_readout_candidates(xqr, sxr, wh, swh, cand3, logits=lg3))
+        torch.cuda.synchronize()
+        cand_us = t.mean_us("cand")
+        # back to back: 50 launches queued behind six full read-outs (about
+        # 1.1 ms of device work, longer than the host takes to enqueue them)
+        cand_b2b = []
+        for _ in range(3):
+            for _ in range(6):
+                B.w8a8_gemm(xqr, sxr, wh, swh, y=yfull)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                B.w8a8_readout_candidates(xqr, sxr, wh, swh, cand3, logits=lg3)
+            e1.record()
+            torch.cuda.synchronize()
+            cand_b2b.append(1e3 * e0.elapsed_time(e1) / 50)
+        cand_b2b_us = float(np.median(cand_b2b))
         readout = {"bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(full_gbs / PEAK_HBM_GBS, 4), "us": round(full_us, 1),
                    "shape": [int(Mr), head["N"], head["K"]], "kernel": "gemm_skinny",
-                   "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"), **readout}
-        del yfull
+                   "traffic": measured_traffic("gemm_full_vocab_readout", "gemm_skinny"),
+                   "candidates_us": round(cand_us, 2), "candidates_us_back_to_back": round(cand_b2b_us, 2),
+                   "candidates_shape": [int(x) for x in rd["cand"].shape],
+                   "candidates_speedup_vs_full": round(full_us / cand_b2b_us, 1), **readout}
+        del yfull, lg3
 
     best_read = None
     if "stream" in legs:

@@ -426,7 +426,16 @@ int check_readout_args(const int8_t* xq, const float* sx, int64_t M, int64_t K, 
 int run_readout(const int8_t* xq, const float* sx, int64_t M, int64_t K, const int8_t* w_vocab,
                 const float* sw_vocab, int64_t V, const int32_t* cand, int64_t C, float* logits,
                 int32_t* err_flag, hipStream_t s) {
-    // 64 answer rows per launch; each launch gathers M_chunk * C weight rows.
+    // One workgroup per row (the answer head's candidate scoring) where the
+    // row fits its registers: 3 rows x 4 candidates of a 5120-wide lm_head
+    // take 3.3 us per launch back to back against 4.9 us on the skinny
+    // kernel, 64 rows x 16 candidates 6.9 against 16.3 us.
+    if (w8a8::answer_head_fused_fits(K)) {
+        const w8a8::ReadoutRowsArgs a{xq, sx, M, K, w_vocab, sw_vocab, V, cand, C, logits, err_flag};
+        return hip_status(w8a8::launch_readout_rows(a, s));
+    }
+    // Otherwise the skinny kernel, 64 answer rows per launch; each launch
+    // gathers M_chunk * C weight rows.
     for (int64_t m0 = 0; m0 < M; m0 += w8a8::SKINNY_MAX_M) {
         const int64_t mc = (M - m0 < w8a8::SKINNY_MAX_M) ? (M - m0) : w8a8::SKINNY_MAX_M;
         w8a8::SkinnyArgs a{xq + m0 * K, sx + m0, w_vocab, sw_vocab, nullptr, logits + m0 * C,

@@ -132,8 +132,8 @@ hipError_t launch_requantize_q8_0(const int8_t* q, const uint16_t* d, const floa
 
 // The answer head in one launch (answer_head.hip): quantise the hidden rows
 // rows[0..M) of h, score the C candidates of each, candidate softmax; the
-// same bits as launch_quantize + launch_skinny (gather/owner mode) +
-// launch_candidate_softmax.  Needs K <= 18432 (answer_head_fused_fits).
+// same bits as launch_quantize + launch_readout_rows (or launch_skinny in
+// gather/owner mode) + launch_candidate_softmax.  Needs K <= 18432 (answer_head_fused_fits).
 struct AnswerHeadArgs {
     const float* h;
     int64_t ldh;
@@ -155,6 +155,25 @@ struct AnswerHeadArgs {
 };
 bool answer_head_fused_fits(int64_t K);
 hipError_t launch_answer_head(const AnswerHeadArgs& a, hipStream_t stream);
+
+// The candidate read-out on given codes (answer_head.hip): one workgroup per
+// row scores its C <= 64 candidates with the answer head's code; the same
+// bits as launch_skinny in gather/owner mode.  Needs K <= 18432
+// (answer_head_fused_fits).
+struct ReadoutRowsArgs {
+    const int8_t* xq;
+    const float* sx;
+    int64_t M;
+    int64_t K;
+    const int8_t* w;
+    const float* sw;
+    int64_t V;
+    const int32_t* cand;
+    int64_t C;
+    float* logits;
+    int32_t* err_flag;
+};
+hipError_t launch_readout_rows(const ReadoutRowsArgs& a, hipStream_t stream);
 
 // Candidate softmax in binary64, one fixed operation sequence (softmax.hip):
 // probs[m, c] for c < C <= 64; rows with a non-finite logit give NaN.

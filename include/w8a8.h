@@ -201,8 +201,10 @@ int w8a8_gemm_splitk_noalloc(const int8_t* xq, const float* sx, const int8_t* w,
  * candidate tokens.
  *     logits[m,c] = fl(fl(float(sum_k xq[m,k]*w_vocab[cand[m,c],k]) * sx[m]) * sw_vocab[cand[m,c]])
  * This is bit-identical to column cand[m,c] of
- * w8a8_gemm(xq, sx, w_vocab, sw_vocab, NULL, ...) (no residual).  It runs on
- * the skinny-GEMM kernel, with the weight rows gathered through `cand`.
+ * w8a8_gemm(xq, sx, w_vocab, sw_vocab, NULL, ...) (no residual).  For
+ * K <= 18432 one workgroup per row computes its C dot products (the answer
+ * head's code); for larger K the skinny-GEMM kernel runs, with the weight
+ * rows gathered through `cand`.
  *
  * xq, sx      device int8 [M,K] (16-byte aligned) and fp32 [M]; usually the
  *             answer rows, picked with w8a8_quantize_act's row_idx.

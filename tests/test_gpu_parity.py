@@ -455,9 +455,14 @@ def test_readout_equals_full_columns_and_oracle():
     assert_bits_equal(logits, want, "cand vs oracle")
 
 
-@pytest.mark.parametrize("M,C", [(1, 1), (5, 64), (70, 3), (130, 17)])
-def test_readout_shapes(M, C):
-    V, K = 3000, 256
+# K <= 18432 runs one workgroup per row (256 threads up to K = 2048, 512
+# above), larger K the skinny kernel's gather mode: both, and each launch
+# shape's edges
+@pytest.mark.parametrize("M,C,K", [(1, 1, 256), (5, 64, 256), (70, 3, 256), (130, 17, 256), (3, 4, 1024),
+                                   (2, 5, 2048), (4, 7, 2112), (3, 4, 5120), (6, 33, 18432), (3, 4, 18496),
+                                   (5, 64, 20480), (70, 3, 40960)])
+def test_readout_shapes(M, C, K):
+    V = 3000
     head = synth.lm_head(V=V, K=K, base=57, layer=0)
     rng = np.random.default_rng(M * C)
     xq = rng.integers(-127, 128, (M, K), dtype=np.int8)
@@ -468,8 +473,9 @@ def test_readout_shapes(M, C):
     assert_bits_equal(got, want, f"readout M={M} C={C}")
 
 
-def test_readout_bad_ids_flagged():
-    V, K = 1000, 128
+@pytest.mark.parametrize("K", [128, 5120, 20480])
+def test_readout_bad_ids_flagged(K):
+    V = 1000
     head = synth.lm_head(V=V, K=K, base=58, layer=0)
     rng = np.random.default_rng(1)
     xq = rng.integers(-127, 128, (2, K), dtype=np.int8)
