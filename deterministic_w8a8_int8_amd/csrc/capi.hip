@@ -120,6 +120,14 @@ bool pick_skinny(int64_t M, int64_t N, int64_t K, bool residual, w8a8::PanelPlan
     const int ov = w8a8::tile_override_value();
     if (ov == w8a8::SKINNY_OVERRIDE) return true;
     if (ov < 0 && w8a8::skinny_streams_lds(M, N, K)) return true;
+    // Narrow layers of a few rows with a long K: the skinny kernel splits K
+    // over the waves of each column tile, where the panel kernel's few panels
+    // each run the whole K (1 x 1024 x 17408: 12 against 32 us; 8 x 5120 x
+    // 17408: 30 against 34 us; 4 x 4096 x 5120: 13.0 against 14.7 us).
+    // Measured over M = 1..16, N = 1024..15360 and K = 2048..17408: below
+    // K = 4096 both are launch-bound, and past N = 8192 or M * N = 65536 the
+    // panel kernel is as fast or faster.
+    if (ov < 0 && K >= 4096 && N <= 8192 && M * N <= 65536) return true;
     *panel = pick_panel(M, N, K, 1, residual, pp);
     return !*panel;
 }

@@ -262,24 +262,25 @@ def test_routing_crossover_matches_oracle(M, N, K, path):
     assert_bits_equal(got[mi, ni], want, f"gemm {M}x{N}x{K} (path {path})")
 
 
-# The skinny kernel forced for M <= 64 (by default those shapes run on the
-# column-panel kernel, which is faster there, and the skinny kernel keeps the
-# full-vocabulary read-out and the candidate gather): its register-streamed
-# weights, the K-parallel mode and ragged tiles, bit for bit.
+# The skinny kernel forced for M <= 64 (by default most of those shapes run
+# on the column-panel kernel, which is faster there; the skinny kernel keeps
+# the full-vocabulary read-out and narrow long-K layers of a few rows): its
+# register-streamed weights, the K-parallel mode and ragged tiles, bit for
+# bit, and the panel kernel forced on the same shapes.
 @pytest.mark.parametrize("M,N,K", SMALL_M)
 @pytest.mark.parametrize("residual", [False, True])
 def test_skinny_kernel_forced_matches_oracle(M, N, K, residual):
     say(f"skinny forced M={M} N={N} K={K} residual={residual}")
     xq, sx, w, sw, r = _gemm_case(M, N, K, seed=M + N + K, residual=residual)
     want = oracle.gemm(xq, sx, w, sw, r)
-    assert B.w8a8_gemm_plan(M, N, K, 1, residual)[0] == 2   # panel by default
-    B.set_tile_override(B.W8A8_TILE_OVERRIDE_SKINNY)
-    try:
-        assert B.w8a8_gemm_plan(M, N, K, 1, residual)[0] == 0
-        got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
-    finally:
-        B.set_tile_override(-1)
-    assert_bits_equal(got, want, f"skinny forced {M}x{N}x{K}")
+    for kind, path, name in ((B.W8A8_TILE_OVERRIDE_SKINNY, 0, "skinny"), (B.W8A8_TILE_OVERRIDE_PANEL, 2, "panel")):
+        B.set_tile_override(kind)
+        try:
+            assert B.w8a8_gemm_plan(M, N, K, 1, residual)[0] == path
+            got = host(B.w8a8_gemm(dev(xq), dev(sx), dev(w), dev(sw), residual=dev(r)))
+        finally:
+            B.set_tile_override(-1)
+        assert_bits_equal(got, want, f"{name} forced {M}x{N}x{K}")
 
 
 # At least 1024 column tiles and activation rows that fit in LDS: the weight

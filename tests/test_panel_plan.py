@@ -172,7 +172,9 @@ def test_panel_default_range():
     """By default the panel kernel takes M <= 384, except full products with
     M <= 16 whose weights the skinny kernel
     streams through LDS (the full-vocabulary read-out): at least 1024 column
-    tiles and M rows of K + 16 bytes within 40 KiB.  From 385 to 1024 rows
+    tiles and M rows of K + 16 bytes within 40 KiB; and narrow layers of a
+    few rows with K >= 4096 (N <= 8192, M * N <= 65536), where the skinny
+    kernel splits K over its waves.  From 385 to 1024 rows
     the two kernels' time models decide (the decisions below are the faster
     kernel as measured on MI355X); past 1024 rows the tiled kernel runs."""
     assert B.w8a8_gemm_plan(1, 4096, 1024, 1, 0)[0] == 2
@@ -182,6 +184,14 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(8, 16384, 5120, 1, 0)[0] == 2    # 8 do not
     assert B.w8a8_gemm_plan(7, 16368, 5120, 1, 0)[0] == 2    # 1023 column tiles
     assert B.w8a8_gemm_plan(3, 248000, 5120, 2, 0)[0] == 2   # split-K: not the skinny kernel
+    # narrow long-K layers of a few rows: the skinny kernel splits K over waves
+    assert B.w8a8_gemm_plan(1, 1024, 17408, 1, 1)[0] == 0
+    assert B.w8a8_gemm_plan(8, 5120, 17408, 1, 1)[0] == 0
+    assert B.w8a8_gemm_plan(12, 5120, 5120, 1, 0)[0] == 0
+    assert B.w8a8_gemm_plan(16, 4096, 17408, 1, 0)[0] == 0
+    assert B.w8a8_gemm_plan(16, 5120, 17408, 1, 1)[0] == 2   # M * N past 65536
+    assert B.w8a8_gemm_plan(4, 10240, 5120, 1, 0)[0] == 2    # N past 8192
+    assert B.w8a8_gemm_plan(1, 4096, 2048, 1, 0)[0] == 2     # K below 4096: launch-bound either way
     assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(512, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(513, 4096, 1024, 1, 0)[0] == 2
