@@ -26,6 +26,10 @@
 // quantisation starts, so their latency overlaps the row's; the workgroup
 // then walks the candidates in groups of AH_GROUP, each group's weights in
 // flight while the previous group is reduced.
+//
+// The candidate scoring is also the candidate read-out itself
+// (w8a8_readout_candidates for K <= 18432): readout_rows_kernel runs it on
+// codes that are already quantised, one workgroup per row.
 #include "device_common.h"
 #include "launch.h"
 #include "quantize_row.h"
