@@ -77,8 +77,9 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 }
 
 // Kernel choice for a full product.  The column-panel kernel takes M up to
-// kPanelOnlyM, and up to kPanelMaxM unless the tiled kernel's time model is
-// clearly faster (see pick_panel), except full products with M <= SKINNY_MAX_M whose weights the
+// kPanelOnlyM, up to kPanelCloseM unless the tiled kernel's time model is
+// clearly faster, and up to kPanelMaxM where its own model is faster (see
+// pick_panel), except full products with M <= SKINNY_MAX_M whose weights the
 // skinny kernel streams through LDS (the full-vocabulary read-out), where
 // the skinny kernel is faster; larger M takes the tiled kernel.  Measured:
 // for M = 16..64 the panel kernel runs 1.5-3.2x faster than the skinny one
@@ -87,7 +88,8 @@ int check_gemm_args(const int8_t* xq, const float* sx, const int8_t* w, const fl
 // The override can force a tiled configuration (0..TILE_KINDS-1), the panel
 // kernel (PANEL_OVERRIDE, any M it fits) or the skinny kernel
 // (SKINNY_OVERRIDE, every M <= SKINNY_MAX_M).
-constexpr int64_t kPanelMaxM = 1024;
+constexpr int64_t kPanelMaxM = 1536;
+constexpr int64_t kPanelCloseM = 1024;   // past here the panel kernel needs the better estimate outright
 constexpr int64_t kPanelOnlyM = 384;   // up to here no comparison: the panel kernel won on every measured shape
 static_assert(W8A8_TILE_OVERRIDE_PANEL == w8a8::PANEL_OVERRIDE, "header and library disagree on the panel override");
 static_assert(W8A8_TILE_OVERRIDE_SKINNY == w8a8::SKINNY_OVERRIDE, "header and library disagree on the skinny override");
@@ -106,9 +108,15 @@ bool pick_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, 
     // launch-bound.  Calibrated on 30 shapes of 384-1024 rows (N from 4096
     // to 34816, K from 256 to 17408, split-K 1 and 8): the rule picks the
     // faster kernel on every one.
-    if (ov < 0 && M > kPanelOnlyM && pp->est_us > 40.0 &&
-        w8a8::tiled_time_estimate_us(M, N, K, max_splitk) < 0.75 * pp->est_us)
-        return false;
+    if (ov < 0 && M > kPanelOnlyM) {
+        const double tiled_us = w8a8::tiled_time_estimate_us(M, N, K, max_splitk);
+        if (M <= kPanelCloseM && pp->est_us > 40.0 && tiled_us < 0.75 * pp->est_us) return false;
+        // 1025-1536 rows: the panel kernel only where its estimate is the
+        // lower one (long-K narrow layers: 1536 x 5120 x 17408 + residual,
+        // 154 against 188 us); the same rule past 1536 rows would keep the
+        // 2048-row down projection on panels, 7% slower than tiles
+        if (M > kPanelCloseM && tiled_us <= pp->est_us) return false;
+    }
     return true;
 }
 

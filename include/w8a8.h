@@ -141,7 +141,7 @@ size_t w8a8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int spl
  * most `splitk` contiguous chunks (review page, section "Bitwise
  * consistency is not lossless quantization": split-K partial sums stay
  * integers).  With S chunks (S = splitk on the tiled kernel; the column-panel
- * kernel, which runs most products of up to 1024 rows, picks S <= splitk for
+ * kernel, which runs most products of up to 1536 rows, picks S <= splitk for
  * speed; w8a8_gemm_plan reports which):
  *     chunk c covers k in [c*Kc, min((c+1)*Kc, K)), Kc = ceil(K/S)
  *     rounded up to a multiple of 64 (of 128 on the panel kernel);

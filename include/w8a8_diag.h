@@ -37,8 +37,8 @@ extern "C" {
  * W8A8_TILE_OVERRIDE_PANEL forces the column-panel kernel wherever it can
  * hold the rows (by default it runs for M <= 384, except the M <= 16 full
  * products whose weights the skinny kernel streams through LDS, and for
- * 385 <= M <= 1024 unless a time model puts the tiled kernel clearly ahead,
- * as for wide layers whose panels would need two rounds of workgroups);
+ * 385 <= M <= 1536 unless the time models put the tiled kernel ahead, as
+ * for wide layers whose panels would need two rounds of workgroups);
  * W8A8_TILE_OVERRIDE_SKINNY forces the skinny kernel for every M <= 64 at
  * split-K 1.  It never changes a result bit, only speed.
  * Returns W8A8_ERR_INVALID_ARG for other values. */

@@ -224,7 +224,7 @@ SHAPES = [
     (3, 300, 2048), (40, 500, 2560), (5, 40, 4096), (16, 1000, 5120),  # (skinny: K split over waves)
     (3, 20, 1024),   # two column tiles: half of the workgroup has no columns (LDS staging regression)
     (65, 100, 64), (200, 257, 192), (300, 520, 1024), (513, 264, 320), (256, 256, 256),
-    (1100, 300, 256), (1537, 70, 448),      # past 1024 rows: the tiled kernel by default
+    (1100, 300, 256), (1537, 70, 448),      # past 1024 rows: the tiled kernel by default (here)
     (48, 20000, 512), (130, 17000, 320),    # narrow-kind panels over many columns
     (40, 34816, 256), (160, 34816, 256),    # wide kinds with the non-temporal weight stream
 ]

@@ -1,7 +1,7 @@
 """GPU parity over seeded random shapes: the whole layer (quantisation, GEMM,
 split-K, epilogue with and without a residual) against the CPU oracle, bit
 for bit, on shapes drawn around the kernels' boundaries: the skinny, panel
-and tiled kernels' row ranges (16, 64, 384, 512 and 1024 rows), ragged row and
+and tiled kernels' row ranges (16, 64, 384, 512, 1024 and 1536 rows), ragged row and
 column tails, K from one 64-byte block to several hundred, split-K from 1 to
 more chunks than K-blocks.  Definitions: review page "StartLux-Prism: Fast,
 exact inference for StartLux-Decision models on NVIDIA GPUs", sections
@@ -23,7 +23,7 @@ if not torch.cuda.is_available():
 from deterministic_w8a8_int8_amd import binding as B  # noqa: E402
 
 # row counts at and around each routing boundary, then anything up to 640
-_M_EDGES = [1, 2, 15, 16, 17, 63, 64, 65, 383, 384, 385, 511, 512, 513, 1023, 1024, 1025]
+_M_EDGES = [1, 2, 15, 16, 17, 63, 64, 65, 383, 384, 385, 511, 512, 513, 1023, 1024, 1025, 1536, 1537]
 
 
 def _shape(rng, i):
@@ -42,7 +42,7 @@ def _wide(rng):
             int(rng.choice([1, 1, 4])), bool(rng.integers(0, 2)))
 
 
-CASES = [_shape(np.random.default_rng(9000 + i), i) for i in range(39)] + \
+CASES = [_shape(np.random.default_rng(9000 + i), i) for i in range(41)] + \
         [_wide(np.random.default_rng(9100 + i)) for i in range(10)]
 
 

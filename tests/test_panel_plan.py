@@ -176,7 +176,9 @@ def test_panel_default_range():
     few rows with K >= 4096 (N <= 8192, M * N <= 65536), where the skinny
     kernel splits K over its waves.  From 385 to 1024 rows
     the two kernels' time models decide (the decisions below are the faster
-    kernel as measured on MI355X); past 1024 rows the tiled kernel runs."""
+    kernel as measured on MI355X); from 1025 to 1536 rows the panel kernel
+    runs only where its estimate is the lower one; past 1536 rows the tiled
+    kernel runs."""
     assert B.w8a8_gemm_plan(1, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(64, 4096, 1024, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(3, 248000, 5120, 1, 0)[0] == 0
@@ -203,7 +205,13 @@ def test_panel_default_range():
     assert B.w8a8_gemm_plan(1024, 5120, 17408, 1, 1)[0] == 2
     assert B.w8a8_gemm_plan(1024, 5120, 17408, 8, 1)[0] == 2
     assert B.w8a8_gemm_plan(1024, 5120, 5120, 1, 0)[0] == 2
-    assert B.w8a8_gemm_plan(1025, 5120, 17408, 1, 1)[0] == 1
+    assert B.w8a8_gemm_plan(1280, 5120, 17408, 1, 1)[0] == 2   # 1025-1536 rows: the panel estimate must win
+    assert B.w8a8_gemm_plan(1536, 5120, 17408, 1, 1)[0] == 2
+    assert B.w8a8_gemm_plan(1280, 34816, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(1536, 15360, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(1536, 5120, 5120, 1, 0)[0] == 1
+    assert B.w8a8_gemm_plan(1537, 5120, 17408, 1, 1)[0] == 1
+    assert B.w8a8_gemm_plan(2048, 5120, 17408, 1, 1)[0] == 1
     assert B.w8a8_gemm_plan(384, 34816, 5120, 1, 0)[0] == 2
     assert B.w8a8_gemm_plan(385, 34816, 5120, 1, 0)[0] == 1
     assert B.w8a8_gemm_plan(512, 34816, 5120, 1, 0)[0] == 1
