@@ -35,9 +35,11 @@ def _quant_case(M, K, seed, n_out=3, mult=30.0):
 # ------------------------------------------------------------------ quantisation
 
 # (1543, 5120) and (2357, 17408): more rows than workgroups resident at once
-# (several rounds of workgroups), with ragged remainders
+# (several rounds of workgroups), with ragged remainders; up to 64 rows with
+# 2048 < K <= 6144 take the wider few-row workgroups (1024 or 512 threads)
 @pytest.mark.parametrize("M,K", [(1, 64), (16, 256), (37, 1024), (300, 5120), (5, 17408), (2, 40960),
-                                 (1543, 5120), (2357, 17408)])
+                                 (1543, 5120), (2357, 17408), (1, 2112), (64, 4096), (3, 5120), (40, 6144),
+                                 (65, 6144)])
 def test_quantize_matches_oracle(M, K):
     say(f"quantize M={M} K={K}")
     x, s = _quant_case(M, K, seed=M * 7 + K)
