@@ -60,3 +60,29 @@ def test_requantised_weights_through_the_layer():
     ow, osw = oracle.requantize_q8_0(q, d, s)
     oxq, osx = oracle.quantize_act(x, s)
     assert_bits_equal(y, oracle.gemm(oxq, osx, ow, osw), "layer on requantised weights")
+
+
+def test_requantize_half_integer_quotients():
+    # quotients w'/sw exactly on half-integers (ties to even) and a few ulps
+    # either side of them: the cases where one rounding of the quotient
+    # decides the code.  Column 0 holds the row maximum 127 * d with s = 1, so
+    # sw = d exactly; odd codes on columns smoothed by 0.5 give q/2.
+    rng = np.random.default_rng(21)
+    N, K = 64, 2048
+    q = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    q[:, 0] = 127
+    q[:, 1::2] |= 1
+    d = np.repeat(rng.uniform(1e-4, 1e-2, (N, 1)), K // 32, axis=1).astype(np.float16)
+    s = np.ones(K, np.float32)
+    s[1::2] = 0.5
+    s[3::8] = np.nextafter(np.float32(0.5), np.float32(1))
+    s[5::8] = np.nextafter(np.float32(0.5), np.float32(0))
+    s[7::16] = np.float32(0.5) * np.float32(1 + 2.0 ** -13)
+    say(f"requantize ties N={N} K={K}")
+    w, sw = B.w8a8_requantize_q8_0(dev(q), dev(d.view(np.uint16).view(np.int16)), dev(s))
+    ow, osw = oracle.requantize_q8_0(q, d.view(np.uint16), s)
+    assert np.array_equal(osw, d[:, 0].astype(np.float32))
+    ties = ow[:, s == np.float32(0.5)].astype(np.int64)
+    assert ties.size and np.all(ties % 2 == 0)        # the fixture really ties
+    assert_bits_equal(host(sw), osw, "sw")
+    np.testing.assert_array_equal(host(w), ow)
