@@ -27,7 +27,13 @@ def _case(seed, N, K):
     return q, d.view(np.uint16), s
 
 
-@pytest.mark.parametrize("N,K", [(1, 64), (37, 1024), (300, 5120), (9, 17408)])
+# one shape per kernel configuration: a wave per row with 1..6 chunks a lane
+# (64, 1088 with lanes past the row, 5120, 6144), a workgroup per row
+# (6208: 2 chunks a lane; 17408: 5, the last block partly past the row;
+# 24576: 6) and the two-pass long-row kernel (24640); row counts that are
+# not multiples of the four rows a workgroup takes
+@pytest.mark.parametrize("N,K", [(1, 64), (5, 64), (37, 1024), (3, 1088), (300, 5120), (6, 6144), (7, 6208),
+                                 (9, 17408), (2, 24576), (3, 24640)])
 def test_requantize_matches_oracle(N, K):
     say(f"requantize N={N} K={K}")
     q, d, s = _case(N + K, N, K)
@@ -37,13 +43,47 @@ def test_requantize_matches_oracle(N, K):
     np.testing.assert_array_equal(host(w), ow)
 
 
-def test_requantize_in_place():
-    q, d, s = _case(5, 40, 2048)
+@pytest.mark.parametrize("N,K", [(40, 2048), (6, 17408), (5, 24640)])
+def test_requantize_in_place(N, K):
+    q, d, s = _case(5, N, K)
     ow, osw = oracle.requantize_q8_0(q, d, s)
     qd = dev(q)
     w, sw = B.w8a8_requantize_q8_0(qd, dev(d.view(np.int16)), dev(s), w=qd)
     np.testing.assert_array_equal(host(qd), ow)
     assert_bits_equal(host(sw), osw, "sw in place")
+
+
+@pytest.mark.parametrize("big", [True, False])
+def test_requantize_scale_extremes(big):
+    # channel scales on both sides of 2^120 and of 2^-120, where the division
+    # by the row's reciprocal stops being exact and every value goes through
+    # the true division instead (and, for the small ones, subnormal w')
+    rng = np.random.default_rng(31 + big)
+    N, K = 12, 1024
+    q = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    q[:, 0] = 127
+    u = rng.uniform(0.25, 1.0, K).astype(np.float32)
+    u[0] = 1.0
+    if big:    # w' = d q 2^121 u: sw = d 2^121 for the row maximum 127 d 2^121
+        s = (u * np.float32(2.0 ** 121)).astype(np.float32)
+        dr = np.float16([1.0, 0.5, 0.5, 0.25, 0.75, 1.0, 0.5, 0.375, 0.5, 0.999, 0.5, 0.5])
+        q[2, 0] = 126      # sw just below 2^120
+        q[6, 0] = -127
+        q[10, 0] = 125
+    else:      # w' = d q 2^-104 u: sw = d 2^-104, subnormal (and so are some w') for d = 2^-24
+        s = (u * np.float32(2.0 ** -104)).astype(np.float32)
+        dr = np.float16([2.0 ** -16, 2.0 ** -17, 2.0 ** -24, 2.0 ** -15, 2.0 ** -16 * 1.5, 2.0 ** -18,
+                         2.0 ** -16, 2.0 ** -23, 2.0 ** -16 * 0.75, 2.0 ** -14, 2.0 ** -16, 2.0 ** -24 * 3])
+        q[6, 0] = 126      # sw just below 2^-120
+    d = np.repeat(dr[:, None], K // 32, axis=1).astype(np.float16)
+    say(f"requantize scale extremes big={big}")
+    w, sw = B.w8a8_requantize_q8_0(dev(q), dev(d.view(np.uint16).view(np.int16)), dev(s))
+    ow, osw = oracle.requantize_q8_0(q, d.view(np.uint16), s)
+    lim = np.float32(2.0 ** 120) if big else np.float32(2.0 ** -120)
+    assert np.any(osw > lim) and np.any(osw < lim) and np.any(osw == lim), osw   # both routes and the edge
+    assert np.all(np.isfinite(osw)) and np.all(osw > 0)
+    assert_bits_equal(host(sw), osw, "sw")
+    np.testing.assert_array_equal(host(w), ow)
 
 
 def test_requantised_weights_through_the_layer():
