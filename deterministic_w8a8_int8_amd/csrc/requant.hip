@@ -10,7 +10,11 @@
 //   w'[n,k] = fl(fl(d[n, k/32] * q[n,k]) * s[k])     (d*q exact in binary32)
 //   sw[n]   = fl(max_k |w'[n,k]| / 127)
 //   wq[n,k] = clamp(rne(fl(w'[n,k] / sw[n])), -127, 127), 0 when sw[n] = 0
-// the same symmetric round-half-even rule as the activations.
+// the same symmetric round-half-even rule as the activations; a row whose w'
+// holds a NaN or an infinity gets sw[n] = NaN and all codes 0, as an
+// activation row that cannot be quantised does.  The row maximum propagates
+// NaNs (v_maximum3_f32, no more instructions than a plain maximum), so such a
+// row shows as a maximum that is not finite.
 //
 // Design.  A one-off pass moving 2 bytes per weight (1 read, 1 written) plus
 // 2 bytes of block scale per 32; the smoothing vector is shared by all rows
@@ -51,6 +55,27 @@ __device__ __forceinline__ float4 smoothed4(uint32_t q4, float d, float4 s) {
     const float w2 = d * static_cast<float>(static_cast<int8_t>((q4 >> 16) & 255u));
     const float w3 = d * static_cast<float>(static_cast<int8_t>(q4 >> 24));
     return make_float4(w0 * s.x, w1 * s.y, w2 * s.z, w3 * s.w);
+}
+
+// Maximum that propagates NaN (IEEE maximum; one v_maximum3_f32 takes two
+// of them with the absolute values).
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float abs_nmax4(float m, float4 w) {
+    const float t = nmax(nmax(m, fabsf(w.x)), fabsf(w.y));
+    return nmax(nmax(t, fabsf(w.z)), fabsf(w.w));
+}
+
+__device__ __forceinline__ float wave_nmax(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = nmax(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// The channel scale of a row maximum m: fl(m / 127), or a NaN (no scale)
+// when m is not finite.
+__device__ __forceinline__ float channel_scale(float m) {
+    return m <= 0x1.fffffep127f ? m / 127.0f : __builtin_nanf("");
 }
 
 // The reciprocal that code_of divides by: fl(1 / sc) for sc in [2^-120,
@@ -146,7 +171,7 @@ __global__ __launch_bounds__(RQ_THREADS) void requantize_rows_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float4 w = smoothed4(static_cast<uint32_t>(qv[c][e]), dv[c], sa[e]);
-                amax = fmaxf(fmaxf(fmaxf(amax, fabsf(w.x)), fmaxf(fabsf(w.y), fabsf(w.z))), fabsf(w.w));
+                amax = abs_nmax4(amax, w);
                 wv[c][4 * e] = w.x;
                 wv[c][4 * e + 1] = w.y;
                 wv[c][4 * e + 2] = w.z;
@@ -157,15 +182,15 @@ __global__ __launch_bounds__(RQ_THREADS) void requantize_rows_kernel(
         for (int e = 0; e < 4; ++e) sa[e] = sb[e];
         __builtin_amdgcn_sched_barrier(0);
     }
-    float m = wave_max(amax);
+    float m = wave_nmax(amax);
     if constexpr (WPR > 1) {
         if (lane == 0) red[wave] = m;
         __syncthreads();
         m = red[0];
 #pragma unroll
-        for (int i = 1; i < WPR; ++i) m = fmaxf(m, red[i]);
+        for (int i = 1; i < WPR; ++i) m = nmax(m, red[i]);
     }
-    const float sc = m / 127.0f;
+    const float sc = channel_scale(m);
     if (lane == 0 && part == 0) sw[n] = sc;
 
     // Pass 2 from the registers.
@@ -175,7 +200,7 @@ __global__ __launch_bounds__(RQ_THREADS) void requantize_rows_kernel(
     for (int c = 0; c < CPL; ++c) {
         if (live(c)) {
             i32x4 packed = {0, 0, 0, 0};
-            if (sc != 0.0f) {   // else an all-zero row (NaNs aside): every code is 0
+            if (sc > 0.0f) {   // else an all-zero row or one without a scale: every code is 0
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     packed[e] = code4(make_float4(wv[c][4 * e], wv[c][4 * e + 1], wv[c][4 * e + 2],
@@ -216,16 +241,16 @@ __global__ __launch_bounds__(RQ_THREADS) void requantize_q8_0_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float4 w = smoothed4(static_cast<uint32_t>(q16[c]), dv, s4[4 * j + c]);
-            amax = fmaxf(fmaxf(fmaxf(amax, fabsf(w.x)), fmaxf(fabsf(w.y), fabsf(w.z))), fabsf(w.w));
+            amax = abs_nmax4(amax, w);
         }
     }
-    amax = wave_max(amax);
+    amax = wave_nmax(amax);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
     __syncthreads();
     float m = red[0];
 #pragma unroll
-    for (int i = 1; i < RQ_WAVES; ++i) m = fmaxf(m, red[i]);
-    const float sc = m / 127.0f;
+    for (int i = 1; i < RQ_WAVES; ++i) m = nmax(m, red[i]);
+    const float sc = channel_scale(m);
     if (threadIdx.x == 0) sw[n] = sc;
     const float inv = recip_or_nan(sc);
     // all of the row's loads above come before any store below (the barrier),
@@ -234,7 +259,7 @@ __global__ __launch_bounds__(RQ_THREADS) void requantize_q8_0_kernel(
     i32x4* out = reinterpret_cast<i32x4*>(wq + n * K);
     for (int64_t j = threadIdx.x; j < K16; j += RQ_THREADS) {
         i32x4 packed = {0, 0, 0, 0};
-        if (sc != 0.0f) {
+        if (sc > 0.0f) {
             const i32x4 q16 = qr[j];
             const float dv = f16_bits_to_f32(dr[j >> 1]);
 #pragma unroll

@@ -234,8 +234,10 @@ int w8a8_readout_candidates(const int8_t* xq, const float* sx, int64_t M, int64_
  *     sw[n]   = fl(max_k |w'[n,k]| / 127)
  *     w[n,k]  = clamp(rne(fl(w'[n,k] / sw[n])), -127, 127)   (0 if sw[n] = 0)
  * The result feeds w8a8_gemm as (w, sw).  The smoothing vector comes from
- * calibration (not done here).  Block scales and smoothing values are
- * finite; a row whose w' holds an infinity or a NaN gets unspecified codes.
+ * calibration (not done here).  A row whose w' holds a NaN or an infinity
+ * (a non-finite block scale or smoothing value, or an overflow) gets
+ * sw[n] = NaN and all codes 0, as an activation row that cannot be quantised
+ * does; a non-finite smoothing value therefore leaves every row so.
  *
  * q       device int8 [N,K] Q8_0 codes, 16-byte aligned; K a multiple of 64.
  * d       device uint16 [N,K/32]: the binary16 bit patterns of the block

@@ -343,7 +343,10 @@ int oracle_gemm_acc(const int8_t* xq, const int8_t* w, int64_t M, int64_t N, int
  *   sw[n]   = fl(max_k |w'[n,k]| / 127)
  *   wq[n,k] = clamp(rne(fl(w'[n,k] / sw[n])), -127, 127), 0 when sw[n] = 0
  * i.e. the same symmetric round-half-even rule as the activations, per
- * output channel.  d is given as binary16 bit patterns. */
+ * output channel.  d is given as binary16 bit patterns.  A row whose w'
+ * holds a NaN or an infinity (a non-finite d or s, or an overflow) has no
+ * scale: sw[n] = NaN and all its codes 0, the activations' rule for a row
+ * that cannot be quantised (the pages say nothing of such inputs). */
 static float oracle_f16_to_f32(uint16_t h) {
     const int sign = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
     float v;
@@ -361,11 +364,18 @@ int oracle_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smoo
 #pragma omp parallel for schedule(static)
     for (n = 0; n < N; ++n) {
         float amax = 0.0f;
+        int finite = 1;
         for (int64_t k = 0; k < K; ++k) {
             float w = oracle_f16_to_f32(d[n * nb + k / 32]) * (float)q[n * K + k];
             float ws = w * smooth[k];
             float ab = fabsf(ws);
+            if (!isfinite(ws)) finite = 0;
             if (ab > amax) amax = ab;
+        }
+        if (!finite) {
+            sw[n] = NAN;
+            for (int64_t k = 0; k < K; ++k) wq[n * K + k] = 0;
+            continue;
         }
         float s = amax / 127.0f;
         sw[n] = s;

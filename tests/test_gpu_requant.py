@@ -126,3 +126,36 @@ def test_requantize_half_integer_quotients():
     assert ties.size and np.all(ties % 2 == 0)        # the fixture really ties
     assert_bits_equal(host(sw), osw, "sw")
     np.testing.assert_array_equal(host(w), ow)
+
+
+def _assert_same_rows(w, sw, ow, osw):
+    assert np.array_equal(np.isnan(sw), np.isnan(osw))
+    fin = ~np.isnan(osw)
+    assert_bits_equal(sw[fin], osw[fin], "sw")
+    np.testing.assert_array_equal(w, ow)
+
+
+@pytest.mark.parametrize("K", [1024, 17408, 24640])
+def test_requantize_non_finite_rows(K):
+    # rows whose w' holds a NaN or an infinity get sw = NaN and all codes 0
+    # (the oracle's rule); the other rows are untouched
+    q, d, s = _case(K + 3, 10, K)
+    d = d.copy()
+    d[0, 1] = 0x7e00                      # a NaN block scale
+    d[1, 2] = 0x7c00                      # +inf with nonzero codes
+    q[1, 64] = 5
+    d[2, 3] = 0xfc00                      # -inf times all-zero codes: NaN
+    q[2, 96:128] = 0
+    d[4, K // 32 - 1] = 0x7bff            # 65504 * 127 * 2^124 overflows, in the last block
+    q[4, K - 3] = 127
+    s[K - 3] = np.float32(2.0 ** 124)
+    say(f"requantize non-finite rows K={K}")
+    w, sw = B.w8a8_requantize_q8_0(dev(q), dev(d.view(np.int16)), dev(s))
+    ow, osw = oracle.requantize_q8_0(q, d, s)
+    assert np.isnan(osw[[0, 1, 2, 4]]).all() and np.isfinite(osw[[3, 5, 6, 7, 8, 9]]).all()
+    _assert_same_rows(host(w), host(sw), ow, osw)
+    s[7] = np.nan                         # now every row
+    w, sw = B.w8a8_requantize_q8_0(dev(q), dev(d.view(np.int16)), dev(s))
+    ow, osw = oracle.requantize_q8_0(q, d, s)
+    assert np.isnan(osw).all()
+    _assert_same_rows(host(w), host(sw), ow, osw)

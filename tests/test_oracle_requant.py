@@ -101,3 +101,46 @@ def test_smoothing_lowers_the_w8a8_error_on_outlier_activations():
         y = oracle.gemm(xq, sx, wq, sw).astype(np.float64)
         err[name] = np.linalg.norm(y - ref) / np.linalg.norm(ref)
     assert err["smoothquant"] < 0.5 * err["none"], err
+
+
+def _nonfinite_rows(q, d_bits, s):
+    """Rows whose smoothed weights d*q*s hold a NaN or an infinity (binary32)."""
+    d = np.repeat(np.asarray(d_bits, np.uint16).view(np.float16).astype(np.float32), 32, axis=1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        wp = (d * q.astype(np.float32)).astype(np.float32) * s
+    return ~np.isfinite(wp).all(axis=1)
+
+
+def test_rows_with_non_finite_smoothed_weights_have_no_scale():
+    # the activations' rule for a row that cannot be quantised: sw = NaN and
+    # every code 0; the other rows are untouched (exact-rational brute force)
+    q, d, rng = _q8_0(11, 8, 128)
+    d = d.copy()
+    s = rng.uniform(0.5, 2.0, 128).astype(np.float32)
+    d[0, 1] = 0x7e00                      # a NaN block scale
+    d[1, 2] = 0x7c00                      # +inf with nonzero codes
+    q[1, 64] = 5
+    d[2, 3] = 0xfc00                      # -inf times all-zero codes: NaN
+    q[2, 96:128] = 0
+    d[3, 0] = 0x7bff                      # 65504 * 127 * 2^124: overflows binary32
+    q[3, 5] = 127
+    s[5] = np.float32(2.0 ** 124)
+    wq, sw = oracle.requantize_q8_0(q, d, s)
+    bad = _nonfinite_rows(q, d, s)
+    assert list(bad) == [True, True, True, True, False, False, False, False]
+    for n in range(8):
+        if bad[n]:
+            assert np.isnan(sw[n]) and not wq[n].any(), n
+        else:
+            codes, swb = _brute_row(q[n], d[n], s)
+            assert sw[n] == np.float32(swb) and list(wq[n]) == codes, n
+
+
+@pytest.mark.parametrize("v", [np.nan, np.inf, -np.inf])
+def test_a_non_finite_smoothing_value_leaves_no_row_a_scale(v):
+    q, d, rng = _q8_0(12, 5, 64)
+    s = rng.uniform(0.5, 2.0, 64).astype(np.float32)
+    s[9] = v                              # w' of column 9 is non-finite in every row
+    wq, sw = oracle.requantize_q8_0(q, d, s)
+    assert _nonfinite_rows(q, d, s).all()
+    assert np.isnan(sw).all() and not wq.any()
