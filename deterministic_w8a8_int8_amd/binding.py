@@ -27,6 +27,7 @@ W8A8_ERR_HIP = -7
 W8A8_MAX_K = 133120
 W8A8_MAX_CANDIDATES = 64
 W8A8_MAX_SPLITK = 64
+W8A8_MAX_ROWS = 4194303
 W8A8_TILE_OVERRIDE_PANEL = 7
 W8A8_TILE_OVERRIDE_SKINNY = 8
 W8A8_NOALLOC_SCRATCH_BYTES = 67108864

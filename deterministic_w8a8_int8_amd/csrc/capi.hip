@@ -27,6 +27,10 @@ int check_k(int64_t K) {
 }
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;  // grid and index limits of the kernels
+// Entry points that launch a workgroup (of up to 1024 threads) per row take
+// at most W8A8_MAX_ROWS rows, so that a launch stays below 2^32 work-items
+// (the dispatch packet's grid size is 32 bits).
+static_assert(int64_t{W8A8_MAX_ROWS} * 1024 < (int64_t{1} << 32), "per-row launches must fit 2^32 work-items");
 
 int hip_status(hipError_t e) { return e == hipSuccess ? W8A8_OK : W8A8_ERR_HIP; }
 
@@ -40,7 +44,7 @@ int check_quantize_args(const float* x, int64_t ldx, int64_t x_rows, const int32
                         const float* smooth, int64_t M, int64_t K, const int8_t* xq, const float* sx) {
     if (M < 0 || x_rows < 0) return W8A8_ERR_INVALID_ARG;
     if (const int kc = check_k(K)) return kc;
-    if (M > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M > W8A8_MAX_ROWS) return W8A8_ERR_SHAPE;
     if (ldx < K || (ldx % 4) != 0) return W8A8_ERR_INVALID_ARG;
     if (!row_idx && M > x_rows) return W8A8_ERR_SHAPE;
     if (M == 0) return W8A8_OK;
@@ -380,7 +384,7 @@ int w8a8_requantize_q8_0(const int8_t* q, const uint16_t* d, const float* smooth
                          int8_t* w, float* sw, void* stream) {
     if (N < 0) return W8A8_ERR_INVALID_ARG;
     if (const int kc = check_k(K)) return kc;
-    if (N > kMaxDim) return W8A8_ERR_SHAPE;
+    if (N > W8A8_MAX_ROWS) return W8A8_ERR_SHAPE;
     if (N == 0) return W8A8_OK;
     if (!q || !d || !smooth || !w || !sw) return W8A8_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(d, 2) || !aligned(smooth, 16) || !aligned(w, 16) || !aligned(sw, 4))
@@ -429,7 +433,7 @@ int check_readout_args(const int8_t* xq, const float* sx, int64_t M, int64_t K, 
     if (M < 0 || C < 0 || V <= 0) return W8A8_ERR_INVALID_ARG;
     if (const int kc = check_k(K)) return kc;
     if (C > W8A8_MAX_CANDIDATES) return W8A8_ERR_TOO_MANY_CANDIDATES;
-    if (M > kMaxDim || V > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M > W8A8_MAX_ROWS || V > kMaxDim) return W8A8_ERR_SHAPE;
     if (M == 0 || C == 0) return W8A8_OK;
     if (!xq || !sx || !w_vocab || !sw_vocab || !cand || !logits) return W8A8_ERR_INVALID_ARG;
     if (!aligned(xq, 16) || !aligned(w_vocab, 16) || !aligned(sx, 4) || !aligned(sw_vocab, 4) ||
@@ -464,7 +468,7 @@ int run_readout(const int8_t* xq, const float* sx, int64_t M, int64_t K, const i
 int check_softmax_args(const float* logits, int64_t M, int64_t C, const double* probs) {
     if (M < 0 || C < 0) return W8A8_ERR_INVALID_ARG;
     if (C > W8A8_MAX_CANDIDATES) return W8A8_ERR_TOO_MANY_CANDIDATES;
-    if (M > kMaxDim) return W8A8_ERR_SHAPE;
+    if (M > W8A8_MAX_ROWS) return W8A8_ERR_SHAPE;
     if (M == 0 || C == 0) return W8A8_OK;
     if (!logits || !probs) return W8A8_ERR_INVALID_ARG;
     if (!aligned(logits, 4) || !aligned(probs, 8)) return W8A8_ERR_ALIGN;

@@ -64,6 +64,12 @@ typedef enum {
 #define W8A8_MAX_CANDIDATES 64
 /* Largest split-K factor accepted. */
 #define W8A8_MAX_SPLITK 64
+/* Most rows per call of the entry points that work row by row: the
+ * quantisations and row maxima (M), the candidate read-out, softmax and
+ * answer head (M) and the requantisation (N).  Above it they return
+ * W8A8_ERR_SHAPE.  (Each such row takes one workgroup; the limit keeps a
+ * launch below 2^32 work-items.) */
+#define W8A8_MAX_ROWS 4194303
 
 /* Human-readable name of a status code (host; never NULL). */
 const char* w8a8_status_string(int status);

@@ -138,6 +138,18 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 64, odd, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_ERR_ALIGN
     assert lib.w8a8_answer_head(p, 64, 8, p, 3, p, 64, p, p, 10, p, 4, p, p, p, odd, nul, S) == B.W8A8_ERR_ALIGN
     assert lib.w8a8_answer_head(p, 64, 8, p, 0, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == B.W8A8_OK
+    # the per-row entry points: at most W8A8_MAX_ROWS rows (one workgroup each)
+    R = B.W8A8_MAX_ROWS
+    assert lib.w8a8_quantize_act(p, 64, R + 1, nul, p, R + 1, 64, p, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_quantize_act(nul, 64, R, nul, p, R, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_row_absmax(p, 64, R + 1, nul, p, R + 1, 64, 0, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_readout_candidates(p, p, R + 1, 64, p, p, 10, p, 4, p, nul, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_readout_candidates(nul, p, R, 64, p, p, 10, p, 4, p, nul, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_candidate_softmax(p, R + 1, 4, ctypes.c_void_p(p.value + (1 << 30)), S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_requantize_q8_0(p, p, p, R + 1, 64, p, p, S) == B.W8A8_ERR_SHAPE
+    assert lib.w8a8_requantize_q8_0(p, p, nul, R, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_answer_head(p, 64, R + 1, p, R + 1, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == \
+        B.W8A8_ERR_SHAPE
     assert lib.w8a8_set_tile_override(99) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_set_tile_override(-2) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_mfma_ceiling(4, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG
