@@ -159,3 +159,31 @@ def test_requantize_non_finite_rows(K):
     ow, osw = oracle.requantize_q8_0(q, d, s)
     assert np.isnan(osw).all()
     _assert_same_rows(host(w), host(sw), ow, osw)
+
+
+def _random_shapes(seed, n):
+    """Seeded (N, K, in_place) cases: K a multiple of 64 up to 30000, drawn
+    half from the neighbourhoods of the kernels' boundaries (one wave per row
+    up to 6144 columns, a workgroup up to 24576, two passes beyond; chunks of
+    1024 columns per wave load)."""
+    rng = np.random.default_rng(seed)
+    edges = [64, 1024, 6144, 24576]
+    out = []
+    for i in range(n):
+        if i % 2:
+            k = int(rng.choice(edges)) + 64 * int(rng.integers(-2, 3))
+        else:
+            k = 64 * int(rng.integers(1, 30000 // 64 + 1))
+        out.append((int(rng.integers(1, 71)), max(64, k), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("N,K,in_place", _random_shapes(2027, 24))
+def test_requantize_random_shapes(N, K, in_place):
+    say(f"requantize random N={N} K={K} in_place={in_place}")
+    q, d, s = _case(N * 7 + K, N, K)
+    ow, osw = oracle.requantize_q8_0(q, d, s)
+    qd = dev(q)
+    w, sw = B.w8a8_requantize_q8_0(qd, dev(d.view(np.int16)), dev(s), w=qd if in_place else None)
+    assert_bits_equal(host(sw), osw, "sw")
+    np.testing.assert_array_equal(host(qd if in_place else w), ow)
