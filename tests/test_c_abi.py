@@ -1,11 +1,11 @@
 """The C ABI used from plain C (tests/c_abi_demo.c): a program that includes
 only include/w8a8.h and the HIP runtime header.  On any host it must compile
-and link against the library; on a GPU it runs quantisation, the GEMM with a
-residual, split-K and the candidate read-out, and checks each output against
-the oracle bit for bit (the definitions of the review page "StartLux-Prism:
-Fast, exact inference for StartLux-Decision models on NVIDIA GPUs", sections
-"Compute shared evidence once" and "Bitwise consistency is not lossless
-quantization")."""
+and link against the library; on a GPU it requantises Q8_0 weights in place,
+runs quantisation, the GEMM with a residual, split-K and the candidate
+read-out on them, and checks each output against the oracle bit for bit (the
+definitions of the review page "StartLux-Prism: Fast, exact inference for
+StartLux-Decision models on NVIDIA GPUs", sections "Compute shared evidence
+once" and "Bitwise consistency is not lossless quantization")."""
 import os
 import shutil
 import subprocess
