@@ -40,6 +40,7 @@ SIGNATURES = {
     "w8a8_abi_version": (_I32, []),
     "w8a8_set_tile_override": (_I32, [_I32]),
     "w8a8_gemm_plan": (_I32, [_I64, _I64, _I64, _I32, _I32, _P]),
+    "w8a8_gemm_panel_forced": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "w8a8_probe_mfma_ceiling": (_I32, [_I32, _I64, _I64, _P, _P, _P]),
     "w8a8_probe_stream_read": (_I32, [_P, _I64, _P, _P]),
     "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
@@ -242,6 +243,26 @@ def w8a8_gemm_splitk(xq, sx, w, sw, splitk, residual=None, y=None, workspace=Non
                                  M, N, K, int(splitk), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "w8a8_gemm_splitk")
+    return y
+
+
+def w8a8_gemm_panel_forced(xq, sx, w, sw, plan, residual=None, y=None, workspace=None, stream=None):
+    """Tuning hook: w8a8_gemm's product on the column-panel kernel with the
+    given plan (configuration, R, P, S); same result bits as w8a8_gemm."""
+    M, N, K = _gemm_shapes(xq, sx, w, sw, residual)
+    kind, R, P, S = (int(v) for v in plan)
+    y = _out(y, (M, N), torch.float32, xq.device, stream, "y")
+    need = w8a8_gemm_splitk_workspace_bytes(M, N, K, S) if S > 1 else 0
+    if workspace is None:
+        workspace = _new((max(need, 1),), torch.uint8, xq.device, stream)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    p = (ctypes.c_int32 * 4)(kind, R, P, S)
+    _check(_lib.w8a8_gemm_panel_forced(_ptr(xq), _ptr(sx), _ptr(w), _ptr(sw), _ptr(residual), _ptr(y),
+                                       M, N, K, ctypes.cast(p, ctypes.c_void_p),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)),
+           "w8a8_gemm_panel_forced")
     return y
 
 

@@ -268,6 +268,24 @@ int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, in
     return W8A8_OK;
 }
 
+int w8a8_gemm_panel_forced(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                           const float* residual, float* y, int64_t M, int64_t N, int64_t K,
+                           const int32_t* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan) return W8A8_ERR_INVALID_ARG;
+    if (const int rc = check_gemm_args(xq, sx, w, sw, residual, y, M, N, K)) return rc;
+    if (M == 0 || N == 0) return W8A8_OK;
+    w8a8::PanelPlan pp;
+    if (plan[3] < 1 || plan[3] > W8A8_MAX_SPLITK ||
+        !w8a8::make_panel_plan(M, N, K, plan[0], plan[1], plan[2], plan[3], &pp))
+        return W8A8_ERR_INVALID_ARG;
+    if (pp.S > 1) {
+        const size_t need = w8a8::gemm_workspace_bytes(M, N, pp.S);
+        if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return W8A8_ERR_WORKSPACE;
+    }
+    const GemmArgs a{xq, sx, w, sw, residual, y, M, N, K, nullptr};
+    return hip_status(w8a8::launch_panel(a, pp, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int w8a8_gemm(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
               const float* residual, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
     if (const int rc = check_gemm_args(xq, sx, w, sw, residual, y, M, N, K)) return rc;

@@ -574,6 +574,23 @@ bool panel_plan_valid(int64_t M, int64_t N, int64_t K, const PanelPlan& p) {
     return true;
 }
 
+bool make_panel_plan(int64_t M, int64_t N, int64_t K, int kind, int R, int P, int S, PanelPlan* out) {
+    if (S < 1 || K < 64) return false;
+    const int64_t KB = K / 64;
+    int64_t kps = (KB + S - 1) / S;
+    if (S > 1) kps = (kps + KBS - 1) / KBS * KBS;
+    PanelPlan p{};
+    p.kind = kind;
+    p.R = R;
+    p.P = P;
+    p.S = S;
+    p.kb_per_split = static_cast<int>(kps);
+    p.est_us = 0.0;
+    if (!panel_plan_valid(M, N, K, p)) return false;
+    *out = p;
+    return true;
+}
+
 hipError_t launch_panel(const GemmArgs& a, const PanelPlan& p, void* workspace, hipStream_t stream) {
     if (!panel_plan_valid(a.M, a.N, a.K, p)) return hipErrorInvalidValue;
     int32_t* partials = a.acc_out ? a.acc_out : p.S > 1 ? static_cast<int32_t*>(workspace) : nullptr;

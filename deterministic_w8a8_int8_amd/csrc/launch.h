@@ -89,6 +89,9 @@ struct PanelPlan {
 };
 bool plan_panel(int64_t M, int64_t N, int64_t K, int max_splitk, bool residual, PanelPlan* out);
 bool panel_plan_valid(int64_t M, int64_t N, int64_t K, const PanelPlan& p);
+// A given plan (kind, R, P, S) with the K-blocks per split the planner would
+// use for S; false when the kernel cannot run it on this shape.
+bool make_panel_plan(int64_t M, int64_t N, int64_t K, int kind, int R, int P, int S, PanelPlan* out);
 // Rows-per-wave and columns-per-panel limits (in blocks of 16), staging
 // register sets and LDS slots of a panel kind.
 bool panel_kind_shape(int kind, int* mw, int* nb, int* nset, int* nslot);

@@ -62,6 +62,23 @@ int w8a8_set_tile_override(int kind);
 int w8a8_gemm_plan(int64_t M, int64_t N, int64_t K, int splitk, int residual, int32_t* out);
 
 /*
+ * Tuning hook: run w8a8_gemm_splitk's product on the column-panel kernel
+ * with a given plan instead of the planner's.  plan: host int32[4] =
+ * {configuration, row splits R, column panels P, K splits S}, the fields
+ * out[1..4] of w8a8_gemm_plan for a panel plan; the K-blocks per split are
+ * the planner's for that S.  The result bits are those of w8a8_gemm (the
+ * plan changes only speed).  With S > 1, workspace (device, 256-byte
+ * aligned, caller-owned) must hold w8a8_gemm_splitk_workspace_bytes(M, N,
+ * K, S) bytes (S * M * N int32 partials, rounded up to 256).  Returns
+ * W8A8_ERR_INVALID_ARG for a plan the kernel cannot run on this shape (rows
+ * or columns beyond the configuration, S outside 1..W8A8_MAX_SPLITK),
+ * W8A8_ERR_WORKSPACE for a missing or short workspace, and otherwise the
+ * checks of w8a8_gemm.  Asynchronous on `stream`.
+ */
+int w8a8_gemm_panel_forced(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                           const float* residual, float* y, int64_t M, int64_t N, int64_t K,
+                           const int32_t* plan, void* workspace, size_t workspace_bytes, void* stream);
+/*
  * Diagnostic (not part of the layer): launch an MFMA-only kernel that runs
  * int8 MFMAs on register-resident operands, with no memory traffic, so the
  * caller can time the throughput the int8 matrix cores sustain on a given

@@ -150,6 +150,27 @@ def test_argument_checks_reject_before_launch(lib):
     assert lib.w8a8_requantize_q8_0(p, p, nul, R, 64, p, p, S) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_answer_head(p, 64, R + 1, p, R + 1, p, 64, p, p, 10, p, 4, p, p, p, q, nul, S) == \
         B.W8A8_ERR_SHAPE
+    # forced panel plans: the plan is checked before any launch
+    def plan(*v):
+        return ctypes.cast((ctypes.c_int32 * 4)(*v), ctypes.c_void_p)
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, nul, nul, 0, S) == B.W8A8_ERR_INVALID_ARG
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, plan(99, 1, 1, 1), nul, 0, S) == \
+        B.W8A8_ERR_INVALID_ARG                                     # no such configuration
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, plan(0, 1, 4, 0), nul, 0, S) == \
+        B.W8A8_ERR_INVALID_ARG                                     # S = 0
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, plan(0, 1, 4, 65), nul, 0, S) == \
+        B.W8A8_ERR_INVALID_ARG                                     # S past W8A8_MAX_SPLITK
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 512, 64, 256, plan(0, 1, 4, 1), nul, 0, S) == \
+        B.W8A8_ERR_INVALID_ARG                                     # 32 row blocks > 4 waves x 1
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 4096, 256, plan(0, 1, 2, 1), nul, 0, S) == \
+        B.W8A8_ERR_INVALID_ARG                                     # 128 column blocks > 2 panels x 8
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, plan(0, 1, 4, 2), nul, 0, S) == \
+        B.W8A8_ERR_WORKSPACE                                       # S = 2 without a workspace
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 256, plan(0, 1, 4, 2), p, 1024, S) == \
+        B.W8A8_ERR_WORKSPACE                                       # 2 x 64 x 64 int32 do not fit 1 KiB
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 0, 64, 256, plan(0, 1, 4, 1), nul, 0, S) == B.W8A8_OK
+    assert lib.w8a8_gemm_panel_forced(p, p, p, p, nul, p, 64, 64, 100, plan(0, 1, 4, 1), nul, 0, S) == \
+        B.W8A8_ERR_SHAPE
     assert lib.w8a8_set_tile_override(99) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_set_tile_override(-2) == B.W8A8_ERR_INVALID_ARG
     assert lib.w8a8_probe_mfma_ceiling(4, 1, 1, p, None, S) == B.W8A8_ERR_INVALID_ARG

@@ -238,3 +238,17 @@ def test_panel_default_range():
         assert B.w8a8_gemm_plan(65, 4096, 1024, 1, 0)[0] == 1
     finally:
         B.set_tile_override(-1)
+
+
+def test_forced_plan_sample_in_bounds():
+    """Every forced plan the GPU parity test runs (panel_cases.sample_plans)
+    keeps the kernel's reads, writes and LDS accesses in bounds."""
+    from panel_cases import SHAPES, sample_plans
+    n = 0
+    for M, N, K, _ in SHAPES:
+        good, bad = sample_plans(M, N, K)
+        assert len(good) >= 6 and bad, (M, N, K)
+        for _, t in good:
+            check_plan(M, N, K, t)
+            n += 1
+    assert n >= 24
