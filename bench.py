@@ -665,6 +665,22 @@ def main():
             readout["frac_of_stream_read"] = round(readout["achieved"] / best_read, 4)
         for q in quant.values():
             q["frac_of_stream_read"] = round(q["GBs"] / best_read, 4)
+        # the quantizer's traffic mix alone (4 bytes read, 1 written per
+        # element) at its two sizes, sources rotated over three copies so the
+        # reads come from HBM: the rate any quantizer moving these bytes meets
+        for key, K in (("quantize_h5120", K1), ("quantize_h17408", K2)):
+            srcs = [torch.empty(M * K, dtype=torch.float32, device="cuda").normal_() for _ in range(3)]
+            dst = torch.empty(M * K, dtype=torch.int8, device="cuda")
+            for i in range(3):
+                B.w8a8_probe_stream_narrow(srcs[i], dst)
+            t = Timer(torch)
+            for i in range(30):
+                moved = t.run("n", lambda: B.w8a8_probe_stream_narrow(srcs[i % 3], dst))
+            torch.cuda.synchronize()
+            narrow_gbs = moved / (t.mean_us("n") * 1e-6) / 1e9
+            quant[key]["stream_narrow_GBs"] = round(narrow_gbs, 1)
+            quant[key]["frac_of_stream_narrow"] = round(quant[key]["GBs"] / narrow_gbs, 4)
+            del srcs, dst
 
     mid_m = mid_m_shapes(torch, B, best_read) if "mid_m" in legs else None
     config4 = large_m_config4(torch, B, synth) if "config4" in legs else None

@@ -43,6 +43,7 @@ SIGNATURES = {
     "w8a8_gemm_panel_forced": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "w8a8_probe_mfma_ceiling": (_I32, [_I32, _I64, _I64, _P, _P, _P]),
     "w8a8_probe_stream_read": (_I32, [_P, _I64, _P, _P]),
+    "w8a8_probe_stream_narrow": (_I32, [_P, _I64, _P, _P]),
     "w8a8_quantize_act": (_I32, [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "w8a8_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_splitk_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
@@ -108,6 +109,16 @@ def w8a8_probe_mfma_ceiling(operand_kind, blocks, iters, sink, stream=None) -> i
     _check(_lib.w8a8_probe_mfma_ceiling(int(operand_kind), int(blocks), int(iters), _ptr(sink),
                                         ctypes.byref(ops), _stream(stream)), "w8a8_probe_mfma_ceiling")
     return ops.value
+
+
+def w8a8_probe_stream_narrow(src, dst, stream=None) -> int:
+    """Launch the narrowing-stream diagnostic: src (float32 device tensor, n
+    elements) -> dst (n bytes); returns the bytes moved (5 per element)."""
+    n = src.numel()
+    if src.dtype != torch.float32 or dst.numel() * dst.element_size() < n:
+        raise ValueError("src must be float32 and dst hold one byte per element")
+    _check(_lib.w8a8_probe_stream_narrow(_ptr(src), n, _ptr(dst), _stream(stream)), "w8a8_probe_stream_narrow")
+    return 5 * n
 
 
 def w8a8_probe_stream_read(buf, sink, stream=None) -> int:

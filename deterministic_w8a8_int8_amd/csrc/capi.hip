@@ -225,6 +225,13 @@ int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* 
     return hip_status(w8a8::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int w8a8_probe_stream_narrow(const void* src, int64_t n, void* dst, void* stream) {
+    if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || n <= 0 || (n & 3) ||
+        overlaps(src, static_cast<size_t>(n) * 4, dst, static_cast<size_t>(n)))
+        return W8A8_ERR_INVALID_ARG;
+    return hip_status(w8a8::launch_stream_narrow(src, n, dst, static_cast<hipStream_t>(stream)));
+}
+
 int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int32_t* sink,
                             int64_t* ops, void* stream) {
     if (operand_kind < 0 || operand_kind > 3 || blocks <= 0 || blocks > kMaxDim || iters <= 0 ||

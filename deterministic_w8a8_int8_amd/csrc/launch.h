@@ -183,9 +183,11 @@ hipError_t launch_readout_rows(const ReadoutRowsArgs& a, hipStream_t stream);
 hipError_t launch_candidate_softmax(const float* logits, int64_t M, int64_t C, double* probs,
                                     hipStream_t stream);
 
-// Diagnostic kernels (probes.hip): MFMA-only ceiling and streaming read.
+// Diagnostic kernels (probes.hip): MFMA-only ceiling, streaming read and
+// narrowing stream.
 int64_t mfma_ceiling_ops(int64_t blocks, int64_t iters);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream);
+hipError_t launch_stream_narrow(const void* src, int64_t n_floats, void* dst, hipStream_t stream);
 hipError_t launch_mfma_ceiling(int kind, int64_t blocks, int64_t iters, int32_t* sink,
                                hipStream_t stream);
 

@@ -1,5 +1,6 @@
-// Diagnostics: sustained int8 MFMA throughput with no memory traffic, and
-// a plain streaming read of device memory.
+// Diagnostics: sustained int8 MFMA throughput with no memory traffic, a
+// plain streaming read of device memory, and a narrowing stream (4 bytes
+// read, 1 written per element).
 //
 // The int8 matrix cores of MI355X do not sustain their nominal rate on
 // every operand stream.  With zero or constant operands they run near the
@@ -155,7 +156,43 @@ __global__ __launch_bounds__(READ_THREADS) void stream_read_kernel(const i32x4* 
     if (x == 0x7a5c3e1f) sink[0] = x;
 }
 
+// Narrowing stream, the traffic mix of the activation quantizer with none of
+// its arithmetic: 4 bytes read and 1 byte written per element.  Workgroup b
+// takes its own contiguous chunk of float4s; per iteration each thread
+// issues eight nontemporal 16-byte loads, then eight 4-byte stores (the top
+// byte of each float; a wave instruction stores 256 contiguous bytes, as the
+// quantizer's code stores do).  Nothing else runs, so its rate bounds what
+// any quantizer moving these bytes can sustain on the GPU.
+__global__ __launch_bounds__(READ_THREADS) void stream_narrow_kernel(const i32x4* __restrict__ p,
+                                                                     uint32_t* __restrict__ q, int64_t n16,
+                                                                     int64_t chunk16) {
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk16;
+    const int64_t b1 = b0 + chunk16 < n16 ? b0 + chunk16 : n16;
+    auto narrow = [](const i32x4& v) __attribute__((always_inline)) {
+        return (static_cast<uint32_t>(v[0]) >> 24) | ((static_cast<uint32_t>(v[1]) >> 24) << 8) |
+               ((static_cast<uint32_t>(v[2]) >> 24) << 16) | ((static_cast<uint32_t>(v[3]) >> 24) << 24);
+    };
+    int64_t i = b0 + threadIdx.x;
+    for (; i + (READ_UNROLL - 1) * READ_THREADS < b1; i += READ_UNROLL * READ_THREADS) {
+        i32x4 v[READ_UNROLL];
+#pragma unroll
+        for (int u = 0; u < READ_UNROLL; ++u) v[u] = __builtin_nontemporal_load(p + i + u * READ_THREADS);
+#pragma unroll
+        for (int u = 0; u < READ_UNROLL; ++u) q[i + u * READ_THREADS] = narrow(v[u]);
+    }
+    for (; i < b1; i += READ_THREADS) q[i] = narrow(__builtin_nontemporal_load(p + i));
+}
+
 }  // namespace
+
+hipError_t launch_stream_narrow(const void* src, int64_t n_floats, void* dst, hipStream_t stream) {
+    const int64_t n16 = n_floats / 4;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + READ_THREADS - 1) / READ_THREADS, 256 * 16));
+    const int64_t chunk16 = (n16 + blocks - 1) / blocks;
+    hipLaunchKernelGGL(stream_narrow_kernel, dim3(static_cast<unsigned>(blocks)), dim3(READ_THREADS), 0,
+                       stream, static_cast<const i32x4*>(src), static_cast<uint32_t*>(dst), n16, chunk16);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream) {
     const int64_t n16 = bytes / 16;

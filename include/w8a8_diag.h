@@ -106,6 +106,18 @@ int w8a8_probe_mfma_ceiling(int operand_kind, int64_t blocks, int64_t iters, int
  * Returns W8A8_ERR_INVALID_ARG for a bad argument.  Asynchronous on `stream`.
  */
 int w8a8_probe_stream_read(const void* buf, int64_t bytes, int32_t* sink, void* stream);
+/*
+ * Diagnostic (not part of the layer): the activation quantizer's traffic
+ * mix with none of its arithmetic.  Reads n 4-byte words at src (16-byte
+ * nontemporal loads) and writes n bytes at dst (byte i = the top byte of
+ * word i), each of up to 4096 workgroups of 256 threads streaming its own
+ * contiguous chunk, so the caller can time the rate a 4-read/1-write stream
+ * sustains (use buffers much larger than the 256 MB last-level cache).
+ * src, dst: device, 16-byte aligned, not overlapping; n a positive multiple
+ * of 4.  Returns W8A8_ERR_INVALID_ARG for a bad argument.  Asynchronous on
+ * `stream`.
+ */
+int w8a8_probe_stream_narrow(const void* src, int64_t n, void* dst, void* stream);
 
 #ifdef __cplusplus
 }

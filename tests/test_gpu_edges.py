@@ -118,3 +118,15 @@ def test_zero_rows_give_the_residual(M, N, K):
     xq_o, sx_o = oracle.quantize_act(x, s)
     assert_bits_equal(got, oracle.gemm(xq_o, sx_o, w, sw, r), "zero rows")
     assert_bits_equal(got[::3], r[::3], "zero rows equal the residual")
+
+
+def test_narrowing_stream_probe_writes_each_top_byte():
+    """The narrowing-stream diagnostic (the quantizer's traffic mix) does the
+    work it is timed for: byte i of the output is the top byte of word i,
+    over a length with a ragged last chunk."""
+    n = 4 * 1000003
+    src = torch.randn(n, device="cuda")
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    assert B.w8a8_probe_stream_narrow(src, dst) == 5 * n
+    want = (src.view(torch.int32) >> 24) & 255
+    assert torch.equal(dst.to(torch.int32), want)
