@@ -359,64 +359,113 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
     // Pass i: every wave parks row block i of its accumulators as int32
     // (16 rows x 16*NB columns, rows padded by 4 words); then all threads
     // sweep the 64 parked rows in 16-byte chunks along the rows: whole-line
-    // residual loads and output stores, the fixed epilogue in between.  An
-    // empty K split still writes its zero partial.
+    // output stores, the fixed epilogue in between.  An empty K split still
+    // writes its zero partial.
+    //
+    // Loads and stores retire through one in-order counter, so a load issued
+    // after a store cannot be waited for without waiting for that store too.
+    // The sweep therefore issues no scale load after its first store: the
+    // row and column scales of the workgroup are copied into LDS before the
+    // passes, and the residual is loaded into registers ahead of the stores.
     constexpr int LDR = 16 * NB + 4;   // parked row pitch (int32)
     constexpr int CH = 4 * NB;         // 16-byte chunks per parked row
-    static_assert(64 * LDR * 4 <= NSLOT * STAGE_BYTES, "epilogue staging fits the ring");
+    constexpr int PER = 64 * CH / PANEL_THREADS;   // sweep chunks per thread and pass
+    constexpr int SX_N = 64 * MW;      // rows of a split a workgroup can hold
+    constexpr int SW_N = 16 * NB;
+    static_assert(64 * LDR * 4 + (SX_N + SW_N) * 4 <= NSLOT * STAGE_BYTES, "epilogue staging fits the ring");
     static_assert((64 * CH) % PANEL_THREADS == 0, "whole sweep iterations");
     int32_t* park = reinterpret_cast<int32_t*>(smem);
+    float* s_sw = reinterpret_cast<float*>(smem + 64 * LDR * 4);
+    float* s_sx = s_sw + SW_N;
     const bool vec_ok = (N & 3) == 0 &&
                         (partials || ((reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
                                       (reinterpret_cast<uintptr_t>(residual) & 15) == 0));
     int32_t* part = partials ? partials + static_cast<size_t>(split) * static_cast<size_t>(M) *
                                               static_cast<size_t>(N)
                              : nullptr;
-    const bool sw_vec = (reinterpret_cast<uintptr_t>(sw) & 15) == 0;
+    const int row_base = 16 * rs0;
+    // chunk `it` of this thread in pass i: parked row rr, chunk cc, output (m, n)
+    struct Chunk {
+        int rr, cc, m, n;
+        bool live;
+    };
+    auto chunk_at = [&](int i, int it) __attribute__((always_inline)) {
+        Chunk c;
+        const int q = t + it * PANEL_THREADS;
+        c.rr = q / CH;
+        c.cc = q % CH;
+        const int w = c.rr >> 4, x = c.rr & 15;
+        const int rbw_w = rs0 + w * nrb / 4;
+        const int mw_w = rs0 + (w + 1) * nrb / 4 - rbw_w;
+        c.m = 16 * (rbw_w + i) + x;
+        c.n = c0 + 4 * c.cc;
+        c.live = i < mw_w && c.m < M && 4 * c.cc < 16 * ncb && c.n < N;
+        return c;
+    };
+    // Narrow kinds (the ones long-K residual layers run on) hold every
+    // pass's residual in registers, loaded before the first store; wider
+    // kinds load each pass's residual one pass ahead.
+    constexpr bool RES_ALL = MW * NB <= 16;
+    constexpr int RB = RES_ALL ? MW : 2;
+    float4 rbuf[RB][PER];
+    auto load_residual = [&](int i, float4* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < PER; ++it) {
+            const Chunk c = chunk_at(i, it);
+            if (c.live && vec_ok && c.n + 3 < N)
+                dst[it] = *reinterpret_cast<const float4*>(
+                    residual + static_cast<size_t>(c.m) * static_cast<size_t>(N) + static_cast<size_t>(c.n));
+        }
+    };
     __syncthreads();   // every wave is done with the operand ring
+    if (!part) {
+        for (int j = t; j < SW_N; j += PANEL_THREADS)
+            if (j < 16 * ncb && c0 + j < N) s_sw[j] = sw[c0 + j];
+        for (int j = t; j < SX_N; j += PANEL_THREADS)
+            if (row_base + j < row_end) s_sx[j] = sx[row_base + j];
+        if (residual) {
+            if constexpr (RES_ALL) {
+#pragma unroll
+                for (int i = 0; i < MW; ++i) load_residual(i, rbuf[i]);
+            } else {
+                load_residual(0, rbuf[0]);
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MW; ++i) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
             *reinterpret_cast<i32x4*>(park + (wave * 16 + f_row) * LDR + 16 * j + 4 * (lane >> 4)) = acc[i][j];
         __syncthreads();
+        if constexpr (!RES_ALL)
+            if (!part && residual && i + 1 < MW) load_residual(i + 1, rbuf[(i + 1) & 1]);
 #pragma unroll
-        for (int it = 0; it < 64 * CH / PANEL_THREADS; ++it) {
-            const int c = t + it * PANEL_THREADS;
-            const int rr = c / CH, cc = c % CH;
-            const int w = rr >> 4, x = rr & 15;
-            const int rbw_w = rs0 + w * nrb / 4;
-            const int mw_w = rs0 + (w + 1) * nrb / 4 - rbw_w;
-            const int m = 16 * (rbw_w + i) + x;
-            const int n = c0 + 4 * cc;
-            if (i >= mw_w || m >= M || 4 * cc >= 16 * ncb || n >= N) continue;
-            const i32x4 a = *reinterpret_cast<const i32x4*>(park + rr * LDR + 4 * cc);
+        for (int it = 0; it < PER; ++it) {
+            const Chunk c = chunk_at(i, it);
+            if (!c.live) continue;
+            const int m = c.m, n = c.n;
+            const i32x4 a = *reinterpret_cast<const i32x4*>(park + c.rr * LDR + 4 * c.cc);
             const size_t o = static_cast<size_t>(m) * static_cast<size_t>(N) + static_cast<size_t>(n);
             if (vec_ok && n + 3 < N) {
                 if (part) {
                     *reinterpret_cast<i32x4*>(part + o) = a;
                     continue;
                 }
-                const float sxm = sx[m];
-                float s0, s1, s2, s3;
-                if (sw_vec) {
-                    const float4 s4 = *reinterpret_cast<const float4*>(sw + n);
-                    s0 = s4.x, s1 = s4.y, s2 = s4.z, s3 = s4.w;
-                } else {
-                    s0 = sw[n], s1 = sw[n + 1], s2 = sw[n + 2], s3 = sw[n + 3];
-                }
+                const float sxm = s_sx[m - row_base];
+                const float4 s4 = *reinterpret_cast<const float4*>(s_sw + 4 * c.cc);
                 float4 v;
                 if (residual) {
-                    const float4 r4 = *reinterpret_cast<const float4*>(residual + o);
-                    v.x = scale_acc_residual(a[0], sxm, s0, r4.x);
-                    v.y = scale_acc_residual(a[1], sxm, s1, r4.y);
-                    v.z = scale_acc_residual(a[2], sxm, s2, r4.z);
-                    v.w = scale_acc_residual(a[3], sxm, s3, r4.w);
+                    const float4 r4 = rbuf[RES_ALL ? i : (i & 1)][it];
+                    v.x = scale_acc_residual(a[0], sxm, s4.x, r4.x);
+                    v.y = scale_acc_residual(a[1], sxm, s4.y, r4.y);
+                    v.z = scale_acc_residual(a[2], sxm, s4.z, r4.z);
+                    v.w = scale_acc_residual(a[3], sxm, s4.w, r4.w);
                 } else {
-                    v.x = scale_acc(a[0], sxm, s0);
-                    v.y = scale_acc(a[1], sxm, s1);
-                    v.z = scale_acc(a[2], sxm, s2);
-                    v.w = scale_acc(a[3], sxm, s3);
+                    v.x = scale_acc(a[0], sxm, s4.x);
+                    v.y = scale_acc(a[1], sxm, s4.y);
+                    v.z = scale_acc(a[2], sxm, s4.z);
+                    v.w = scale_acc(a[3], sxm, s4.w);
                 }
                 // non-temporal: every workgroup writes its outputs in the same
                 // burst at the end, and streamed stores drain that burst 5-9%
@@ -427,8 +476,8 @@ __global__ __launch_bounds__(PANEL_THREADS, 1) void gemm_panel(
                 for (int e = 0; e < 4; ++e) {
                     if (n + e >= N) continue;
                     if (part) part[o + e] = a[e];
-                    else y[o + e] = residual ? scale_acc_residual(a[e], sx[m], sw[n + e], residual[o + e])
-                                             : scale_acc(a[e], sx[m], sw[n + e]);
+                    else y[o + e] = residual ? scale_acc_residual(a[e], s_sx[m - row_base], s_sw[4 * c.cc + e], residual[o + e])
+                                             : scale_acc(a[e], s_sx[m - row_base], s_sw[4 * c.cc + e]);
                 }
             }
         }
