@@ -602,6 +602,7 @@ def main():
                "answer_head_us_events_each": kernels.get("answer_head"),
                "answer_head_host_us_per_call": round(float(np.median(head_host)), 2)}
     if "readout" in legs:
+        print("# leg readout", file=sys.stderr, flush=True)
         # full-vocabulary read-out (M = 3 answer rows): HBM-bound skinny GEMM
         Mr = rd["answer_rows"].size
         xqr, sxr = B.w8a8_quantize_act(dev(rd["h"]), sh, row_idx=dev(rd["answer_rows"]))
@@ -649,6 +650,7 @@ def main():
 
     best_read = None
     if "stream" in legs:
+        print("# leg stream", file=sys.stderr, flush=True)
         # streaming read of 4 GiB: the read bandwidth HBM sustains on this GPU
         rbuf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
         rsink = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -682,16 +684,23 @@ def main():
             quant[key]["frac_of_stream_narrow"] = round(quant[key]["GBs"] / narrow_gbs, 4)
             del srcs, dst
 
-    mid_m = mid_m_shapes(torch, B, best_read) if "mid_m" in legs else None
-    config4 = large_m_config4(torch, B, synth) if "config4" in legs else None
-    row_parallel = row_parallel_rank(torch, B, x2, s2, w2, sw2, r2) if "row_parallel" in legs else None
-    graph = short_request_graph(torch, B, synth) if "graph" in legs else None
-    requant = startup_requantize(torch, B, w1, s1, w2, s2) if "requant" in legs else None
+    def leg(name, fn):
+        if name not in legs:
+            return None
+        print(f"# leg {name}", file=sys.stderr, flush=True)
+        return fn()
+
+    mid_m = leg("mid_m", lambda: mid_m_shapes(torch, B, best_read))
+    config4 = leg("config4", lambda: large_m_config4(torch, B, synth))
+    row_parallel = leg("row_parallel", lambda: row_parallel_rank(torch, B, x2, s2, w2, sw2, r2))
+    graph = leg("graph", lambda: short_request_graph(torch, B, synth))
+    requant = leg("requant", lambda: startup_requantize(torch, B, w1, s1, w2, s2))
 
     # sustained MFMA-only ceiling on this GPU for two kinds of operand data and
     # both MFMA forms; the large-M kernel runs 16x16x64
     ceiling = {}
     if "ceiling" in legs:
+        print("# leg ceiling", file=sys.stderr, flush=True)
         sink = torch.zeros(16, dtype=torch.int32, device="cuda")
         for kind, name in ((0, "uniform_int8"), (1, "activation_like"), (2, "uniform_int8_16x16x64"),
                            (3, "activation_like_16x16x64")):
