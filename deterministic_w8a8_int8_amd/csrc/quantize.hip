@@ -98,6 +98,11 @@ __global__ __launch_bounds__(T, WAVES) void quantize_rows_reg(
 
     float scale[R];
     bool valid[R];
+    // The codes are stored after the code pass: its rare exact paths load
+    // smoothing values (without KEEP), and loads and stores retire through
+    // one in-order counter, so a load issued after a store would wait for
+    // that store to complete.
+    uint32_t codes[R][NV];
     quantize_rows_regs<NV, T, R, GIVEN>(
         xv, [&](int i) __attribute__((always_inline)) { return rv[i]; },
         [&](int i, int j) __attribute__((always_inline)) {
@@ -105,10 +110,14 @@ __global__ __launch_bounds__(T, WAVES) void quantize_rows_reg(
             else return s4[j];
         },
         odd_t, K4, ok, amax_g, red,
-        [&](int r, int i, uint32_t packed) __attribute__((always_inline)) {
-            if (live[r]) reinterpret_cast<uint32_t*>(xq + (m0 + r) * K)[t + i * T] = packed;
-        },
+        [&](int r, int i, uint32_t packed) __attribute__((always_inline)) { codes[r][i] = packed; },
         scale, valid);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (live[r] && t + i * T < K4) reinterpret_cast<uint32_t*>(xq + (m0 + r) * K)[t + i * T] = codes[r][i];
+    }
     if (t == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
