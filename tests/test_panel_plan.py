@@ -60,8 +60,8 @@ def check_plan(M, N, K, plan):
     st_lc = (t & 7) ^ swz(t >> 3)
     lane = np.arange(64)
     for lid in lids:
-        r, split, p = lid % R, (lid // R) % S, lid // (R * S)
-        assert p < P
+        r, p, split = lid % R, (lid // R) % P, lid // (R * P)
+        assert p < P and split < S
         cb0 = p * cb_base + min(p, cb_extra)
         ncb = cb_base + (1 if p < cb_extra else 0)
         assert 1 <= ncb <= NB, (ncb, NB)
